@@ -1,0 +1,98 @@
+"""Reference for the two cache-mutating operations: slot scatter and block copy.
+
+TEST INFRASTRUCTURE: part of the CPU oracle.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import it.
+
+* ``cache_write_ref`` is the paged form of appending new K/V to a cache:
+  "推理优化" (section 二, Step 1) writes new keys/values into a contiguous
+  ``[layers, heads, seq, head_dim]`` cache at the next positions; with a
+  paged cache, position t of a sequence lives in slot
+  ``block_table[t // 16] * 16 + t % 16`` ("系统级优化…" section 2.3), so
+  the write becomes a scatter to slots.  A negative slot means "skip".
+  For an fp8 cache each value is stored as the e4m3 code of
+  ``float32(x) / float32(scale[block, head])``, rounded to nearest even and
+  saturated at 448.
+* ``copy_blocks_ref`` is the copy step of copy-on-write: a block shared by
+  several sequences is duplicated when one of them diverges
+  ("17 · 连续批处理与 PagedAttention" section 三, 写时复制的共享;
+  "推理优化" section "PagedAttention").  Each (src, dst) pair copies all
+  KV heads of the K and V blocks, and for fp8 caches the per-(block, head)
+  scales.
+
+Both return new arrays and leave their inputs untouched.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+from .formats import bf16_to_f32, e4m3_quantize
+
+BLOCK = 16
+
+
+def _src_f32(x: np.ndarray, src_dtype: str) -> np.ndarray:
+    if src_dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if src_dtype == "bf16":
+        return bf16_to_f32(x)
+    raise ValueError(f"unsupported source dtype {src_dtype}")
+
+
+def cache_write_ref(k_cache: np.ndarray, v_cache: np.ndarray, new_k: np.ndarray, new_v: np.ndarray,
+                    slot_mapping: np.ndarray, src_dtype: str, cache_dtype: str,
+                    k_scale: Optional[np.ndarray] = None,
+                    v_scale: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Scatter token t's K/V ``[Hkv, D]`` rows into ``cache[slot // 16, :, slot % 16, :]``.
+
+    Tokens are applied in order; slots < 0 are skipped.  For f32 and bf16
+    caches the source must have the cache's type and its bits are copied.
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = int(slot) // BLOCK, int(slot) % BLOCK
+        if cache_dtype in ("f32", "bf16"):
+            if src_dtype != cache_dtype:
+                raise ValueError("f32/bf16 caches take sources of the same type")
+            k_out[blk, :, off, :] = new_k[t]
+            v_out[blk, :, off, :] = new_v[t]
+        elif cache_dtype == "fp8":
+            ks = np.asarray(k_scale, dtype=np.float32)[blk][:, None]
+            vs = np.asarray(v_scale, dtype=np.float32)[blk][:, None]
+            k_out[blk, :, off, :] = e4m3_quantize(_src_f32(new_k[t], src_dtype), ks)
+            v_out[blk, :, off, :] = e4m3_quantize(_src_f32(new_v[t], src_dtype), vs)
+        else:
+            raise ValueError(f"unknown cache dtype {cache_dtype}")
+    return k_out, v_out
+
+
+def quantize_pool_ref(values: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """e4m3 codes of a float32 pool ``[NB, Hkv, 16, D]`` with scales ``[NB, Hkv]``."""
+    out = np.empty(values.shape, dtype=np.uint8)
+    step = max(1, (1 << 22) // max(1, int(np.prod(values.shape[1:]))))
+    for s in range(0, values.shape[0], step):
+        e = min(values.shape[0], s + step)
+        out[s:e] = e4m3_quantize(values[s:e], scales[s:e][:, :, None, None])
+    return out
+
+
+def copy_blocks_ref(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray,
+                    k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None):
+    """Copy block src to block dst for every (src, dst) pair, in order."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    ks = None if k_scale is None else np.array(k_scale, copy=True)
+    vs = None if v_scale is None else np.array(v_scale, copy=True)
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_out[dst] = k_out[src]
+        v_out[dst] = v_out[src]
+        if ks is not None:
+            ks[dst] = ks[src]
+            vs[dst] = vs[src]
+    return k_out, v_out, ks, vs
