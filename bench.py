@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Paged-KV decode benchmark on one MI355X.
+
+One step = one decode step of the Llama-3-8B-shaped layer (64 sequences,
+32 query / 8 KV heads, head_dim 128, bf16, contexts U{128..4096}): the slot
+scatter of the 64 new tokens (pa_cache_write) followed by the paged decode
+(pa_decode: partition kernel + log-sum-exp merge).  Inputs are seeded,
+synthetic and resident in HBM before timing; the K/V pool is rotated over
+several copies so the 256 MB Infinity Cache cannot hold it between steps.
+
+Prints one JSON line: whole-step KV throughput (algorithmic bytes / step
+time), sequences/s, fraction of the 8 TB/s HBM spec and of a measured
+stream-read ceiling, the decode partition kernel's roofline entry (its
+algorithmic bytes over its average duration, from HIP events recorded on
+its own stream during the timed steps), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+SPEC_HBM_GBPS = 8000.0
+METRIC = "paged-decode KV GB/s & % of MI355X HBM peak; seqs/s (8B-shape, bs=64)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_bs64.json")
+KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "paged_kv_cache_272_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pools", type=int, default=3, help="K/V pool copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def measured_stream_read(pa, torch, nbytes=4 << 30, reps=5):
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(pa.pa_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        pa.pa_probe_stream_read(buf, sink)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pa.pa_probe_stream_read(buf, sink)
+        e1.record()
+        e1.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def cpu_baseline(wl, k_ref, v_ref, budget_s):
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        done, t_start = [], time.perf_counter()
+        for b in range(wl.num_seqs):
+            oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16",
+                              seqs=[b])
+            done.append(b)
+            if time.perf_counter() - t_start >= budget_s:
+                break
+        elapsed = time.perf_counter() - t_start
+    lens = wl.context_lens[done]
+    nbytes = oracle.decode_algorithmic_bytes(lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2, 2, 2)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"float64 numpy oracle (decode_ref), BLAS limited to 1 thread, on the first {len(done)} of "
+                  f"{wl.num_seqs} sequences ({int(lens.sum())} tokens, {nbytes / 1e6:.1f} MB algorithmic) "
+                  f"in {elapsed:.1f} s; host CPU {cpu}",
+        "seqs_per_s": round(len(done) / elapsed, 3),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by sequence or KV head with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_272_amd as pa
+    import pa_workloads as W
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    wl = W.config2()
+    gen_s = time.perf_counter() - t_gen
+    print(f"# workload generated in {gen_s:.1f} s: {wl.num_blocks} blocks, sum ctx {int(wl.context_lens.sum())}",
+          file=sys.stderr, flush=True)
+
+    def dev(a, bf16=False):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to("cuda")
+
+    q = dev(wl.q, True)
+    new_k, new_v = dev(wl.new_k, True), dev(wl.new_v, True)
+    bt, cl, slots = dev(wl.block_tables), dev(wl.context_lens), dev(wl.slot_mapping)
+    k0, v0 = dev(wl.k_cache, True), dev(wl.v_cache, True)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
+    out = torch.empty_like(q)
+    part = pa.pa_decode_partition_tokens(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_context_len, args.partition_tokens)
+    ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                           wl.max_context_len, part)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    steps = []
+    for kc, vc in pools:
+        steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
+                      pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale,
+                                        partition_tokens=part, workspace=ws)))
+
+    import oracle
+    decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                                                   wl.head_dim, 2, 2, 2)
+    write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * 2 * 2 * 2 + wl.num_seqs * 8
+    step_bytes = decode_bytes + write_bytes
+
+    peak_meas = measured_stream_read(pa, torch)
+    print(f"# measured stream read {peak_meas:.0f} GB/s", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        w, d = steps[i % len(steps)]
+        w()
+        d()
+    torch.cuda.synchronize()
+
+    pa.pa_timing_read()
+    pa.pa_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w, d = steps[i % len(steps)]
+        w()
+        d()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pa.pa_timing_enable(False)
+    part_ms, merge_ms, calls = pa.pa_timing_read()
+
+    step_s = (t1 - t0) / args.steps
+    value = step_bytes / step_s / 1e9
+    part_avg_ms = part_ms / max(calls, 1)
+    merge_avg_ms = merge_ms / max(calls, 1)
+    achieved = decode_bytes / (part_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)",
+        "config": {
+            "workload": "llama3_8b_shape_decode_bs64",
+            "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": 16, "context_lens": "U{128..4096}",
+            "sum_context": int(wl.context_lens.sum()), "kv_dtype": "bf16", "pool_blocks": wl.num_blocks,
+            "pools_rotated": len(pools), "partition_tokens": part,
+            "step": "pa_cache_write(64 tokens) + pa_decode",
+        },
+        "seqs_per_s": round(wl.num_seqs / step_s, 1),
+        "pct_of_spec_hbm": round(100 * value / SPEC_HBM_GBPS, 2),
+        "measured_stream_read_GBps": round(peak_meas, 1),
+        "pct_of_measured_stream_read": round(100 * value / peak_meas, 2),
+        "step_algorithmic_bytes": int(step_bytes),
+        "decode_partition_kernel_ms": round(part_avg_ms, 5),
+        "decode_merge_kernel_ms": round(merge_avg_ms, 5),
+        "roofline": {
+            "kernel": "decode partition kernel",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": SPEC_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / SPEC_HBM_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(decode_bytes),
+        },
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        k_ref, v_ref = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping,
+                                              "bf16", "bf16")
+        result["cpu_baseline"] = cpu_baseline(wl, k_ref, v_ref, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

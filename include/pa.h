@@ -1,0 +1,210 @@
+/*
+ * pa.h — C ABI of libpa, a paged-KV decode library for AMD MI355X (gfx950).
+ *
+ * The operations follow the paged KV cache described on the pages:
+ *   - "系统级优化：批处理、PagedAttention 与 FlashAttention", section 2.3:
+ *     the KV cache is cut into pages of 16 tokens; a per-request block
+ *     table maps logical pages to physical pages anywhere in a pool.
+ *   - "17 · 连续批处理与 PagedAttention", section 三: physical blocks come
+ *     from a global pool, are reference counted, may be shared, and are
+ *     copied only when a sharer diverges (copy-on-write).
+ *   - "系统级优化…", section 3.1 (attention equation) and 3.3 (scale
+ *     head_dim ** -0.5): out = softmax(q K^T * scale) V.
+ *   - "推理优化", section 五 exercise 3: grouped-query attention, several
+ *     query heads reading one KV head.
+ *
+ * Layouts (row-major, element counts in brackets):
+ *   q, out          [num_seqs, num_q_heads, head_dim]
+ *   k_cache, v_cache [num_blocks, num_kv_heads, 16, head_dim]
+ *   k_scale, v_scale [num_blocks, num_kv_heads] fp32 (fp8 caches only)
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32 physical block ids
+ *   context_lens    [num_seqs] int32
+ *   slot_mapping    [num_tokens] int64, slot = block * 16 + offset, < 0 = skip
+ *   block_pairs     [num_pairs, 2] int32 (src, dst)
+ *
+ * Ownership: every array argument is device memory owned by the caller.
+ * The library allocates no device memory and keeps no per-call state.
+ * All calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ * stream) and return without synchronising.  The return value reports
+ * host-side validation and launch errors only; a fault inside a kernel
+ * surfaces at the caller's next synchronisation.  No C++ exception crosses
+ * this boundary.  Calls are thread-safe.
+ *
+ * Query heads map to KV heads by consecutive groups: query head h reads KV
+ * head h / (num_q_heads / num_kv_heads) (the pages do not fix this mapping).
+ *
+ * The fp8 type is OCP e4m3 ("E4M3FN": bias 7, max 448, no infinities),
+ * gfx950's native 8-bit float.  The pages name "fp8" only as a KV-cache
+ * setting ("17 · 连续批处理与 PagedAttention", section 四).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1,
+  PA_DTYPE_FP8_E4M3 = 2
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = -1, /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = -2,    /* a size is negative, inconsistent or out of range */
+  PA_ERR_BAD_DTYPE = -3,    /* unknown dtype or unsupported dtype combination */
+  PA_ERR_UNSUPPORTED = -4,  /* head_dim or group size outside the supported set */
+  PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_MISALIGNED = -6,   /* a q/out/cache pointer is not 16-byte aligned */
+  PA_ERR_LAUNCH = -7        /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+/*
+ * pa_cache_write — scatter one decode step's new K/V rows into their pages.
+ *
+ * For every token t with slot_mapping[t] >= 0:
+ *   k_cache[slot / 16, h, slot % 16, :] = k[t, h, :]   for every KV head h
+ *   (same for v).
+ * This is the paged form of appending new keys and values to a KV cache
+ * ("推理优化", section 二 Step 1, where new K/V are written after the
+ * current length of a contiguous cache).
+ *
+ * k, v:      [num_tokens, num_kv_heads, head_dim] of src_dtype.
+ * cache_dtype F32 or BF16: src_dtype must equal it; bits are copied.
+ * cache_dtype FP8_E4M3: src_dtype F32 or BF16; each value x is stored as the
+ *   e4m3 code of float32(x) / k_scale[block, h] (IEEE division), rounded to
+ *   nearest even and saturated to +-448.  k_scale/v_scale must be given.
+ * Preconditions not checked on the device: live slots are unique and below
+ * num_blocks * 16 (a slot outside the pool is skipped by the kernel).
+ * Errors: NULL_POINTER, BAD_SHAPE (num_tokens < 0, num_kv_heads < 1,
+ * num_blocks < 1), BAD_DTYPE, UNSUPPORTED (head_dim not 64 or 128),
+ * MISALIGNED, LAUNCH.  num_tokens == 0 is a no-op.
+ */
+int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype,
+                   void* k_cache, void* v_cache, pa_dtype cache_dtype,
+                   const float* k_scale, const float* v_scale,
+                   const int64_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                   void* stream);
+
+/*
+ * pa_decode_partition_tokens — the partition length pa_decode uses.
+ *
+ * Returns `partition_tokens` itself when it is positive, otherwise the
+ * automatic choice for this shape (a multiple of 16).  Returns a negative
+ * pa_status for invalid arguments.
+ */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len,
+                                   int32_t partition_tokens);
+
+/*
+ * pa_decode_workspace_size — bytes of scratch pa_decode needs.
+ *
+ * Zero when every sequence fits one partition (then workspace may be
+ * NULL).  Otherwise room for per-(sequence, query head, partition) partial
+ * results: running max, running sum and an unnormalised fp32 output row.
+ * Returns 0 for invalid arguments as well; pa_decode then reports the error.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len,
+                                int32_t partition_tokens);
+
+/*
+ * pa_decode — one query token per sequence attending over its paged cache.
+ *
+ * For sequence b, query head h, KV head g = h / (num_q_heads/num_kv_heads):
+ *   out[b, h, :] = sum_t softmax_t(scale * q[b,h,:] . K_b[g,t,:]) V_b[g,t,:]
+ * over tokens t < context_lens[b], where token t of sequence b is
+ *   K_b[g, t, :] = k_cache[block_tables[b, t / 16], g, t % 16, :]
+ * (for FP8 caches, times k_scale[block, g]; V likewise with v_scale).
+ * ("系统级优化…" sections 2.3 and 3.1; "17 · 连续批处理与 PagedAttention"
+ * section 三.)  Long contexts are split into partitions of
+ * pa_decode_partition_tokens() tokens whose partial results are merged
+ * exactly by log-sum-exp.  Accumulation is fp32; out has q's dtype and is
+ * rounded to nearest even.  context_lens[b] == 0 gives a zero row.
+ *
+ * Supported: (q F32, cache F32), (q BF16, cache BF16), (q BF16, cache
+ * FP8_E4M3 with k_scale/v_scale); head_dim 64 or 128; num_q_heads a
+ * multiple of num_kv_heads with a group of at most 16.
+ * max_context_len is a host-side upper bound of context_lens (it sizes the
+ * launch) and must not exceed max_blocks_per_seq * 16; partition_tokens is
+ * 0 (automatic) or a positive multiple of 16.
+ * Preconditions not checked on the device: block ids used by a sequence lie
+ * in [0, num_blocks) (the kernel clamps them, so a bad table gives wrong
+ * numbers, not a fault) and context_lens[b] <= max_context_len.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE,
+ * MISALIGNED, LAUNCH.  num_seqs == 0 is a no-op.
+ * pa_decode writes only `out` and `workspace`.
+ */
+int pa_decode(void* out, const void* q, pa_dtype q_dtype,
+              const void* k_cache, const void* v_cache, pa_dtype cache_dtype,
+              const float* k_scale, const float* v_scale,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t max_context_len,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t num_blocks, float scale,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * pa_copy_blocks — the copy step of copy-on-write.
+ *
+ * For every pair i: block block_pairs[i,1] of k_cache and of v_cache becomes
+ * a copy of block block_pairs[i,0] (all KV heads, all 16 slots), and for
+ * FP8 caches k_scale/v_scale[dst, :] = [src, :].  ("17 · 连续批处理与
+ * PagedAttention", section 三: a shared block is copied when a sharer
+ * diverges; "推理优化", section "PagedAttention".)
+ * Preconditions not checked on the device: destinations are unique and no
+ * destination is also a source (pairs run in parallel); ids outside
+ * [0, num_blocks) are skipped.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, MISALIGNED,
+ * LAUNCH.  num_pairs == 0 is a no-op.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
+                   float* k_scale, float* v_scale,
+                   const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                   void* stream);
+
+/* pa_status_string — static text for a status code (never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * Measurement hooks (not part of the method; used to report achieved
+ * bandwidth against the hardware's).
+ *
+ * pa_timing_enable(1) makes pa_decode record HIP events on its stream
+ * around its partition kernel and its merge kernel; pa_timing_read()
+ * waits for the recorded events, returns the summed kernel times in
+ * milliseconds and the number of pa_decode calls recorded, and clears
+ * the record.  At most 65536 calls are recorded between reads.
+ */
+int pa_timing_enable(int enable);
+int pa_timing_read(double* partition_ms, double* merge_ms, int64_t* calls);
+
+/*
+ * pa_probe_stream_read — read `bytes` (a multiple of 16) from `buf` with
+ * 16-byte loads and write one 16-byte checksum per workgroup into `sink`
+ * (at least pa_probe_sink_bytes() bytes), so the loads cannot be elided.
+ * pa_probe_copy — copy `bytes` (a multiple of 16) from src to dst.
+ * Both measure what the memory system sustains for a plain stream.
+ */
+size_t pa_probe_sink_bytes(void);
+int pa_probe_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
+int pa_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,17 @@
+"""Paged-KV decode for AMD MI355X (gfx950): HIP kernels behind a C ABI (include/pa.h).
+
+``import paged_kv_cache_272_amd`` loads the built ``libpa.so`` and fails if
+it is missing; build it with ``python -m paged_kv_cache_272_amd.build``.
+"""
+from ._lib import (BLOCK_SIZE, EXPORTED, LIB_PATH, PA_DTYPE_BF16, PA_DTYPE_F32, PA_DTYPE_FP8_E4M3, PaError,
+                   pa_cache_write, pa_copy_blocks, pa_decode, pa_decode_partition_tokens,
+                   pa_decode_workspace_size, pa_probe_copy, pa_probe_sink_bytes, pa_probe_stream_read,
+                   pa_status_string, pa_timing_enable, pa_timing_read, prepare_cache_write,
+                   prepare_decode)
+
+__all__ = [
+    "BLOCK_SIZE", "EXPORTED", "LIB_PATH", "PA_DTYPE_BF16", "PA_DTYPE_F32", "PA_DTYPE_FP8_E4M3", "PaError",
+    "pa_cache_write", "pa_copy_blocks", "pa_decode", "pa_decode_partition_tokens",
+    "pa_decode_workspace_size", "pa_probe_copy", "pa_probe_sink_bytes", "pa_probe_stream_read",
+    "pa_status_string", "pa_timing_enable", "pa_timing_read", "prepare_cache_write", "prepare_decode",
+]

@@ -1,0 +1,260 @@
+// Generic paged decode (VALU): every supported dtype, head_dim and group size.
+//
+// out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b for one query token per
+// sequence ("系统级优化…", section 3.1), where K_b, V_b are gathered page by
+// page through the block table ("系统级优化…", section 2.3).  Query head h
+// reads KV head h / G (consecutive groups).
+//
+// One workgroup (4 waves) per (partition, KV head, sequence).  A partition
+// is a run of `partition_tokens` tokens; its G query heads' scores live in
+// LDS, so the partition is processed with an exact softmax over its tokens
+// and emitted as (max, sum, unnormalised output) for the merge kernel, or
+// as the final output when the sequence has a single partition.  Logits are
+// kept in the base-2 domain (q is pre-scaled by scale*log2 e).
+//
+// Masking: tokens at or past the context length get a score of -inf by
+// selection, and the P.V loop never touches them, so NaN in unused slots
+// cannot reach the output.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxGroup = 16;
+
+enum KvKind { kKvF32 = 0, kKvBf16 = 1, kKvFp8 = 2 };
+
+template <int KV>
+struct KvTraits;
+template <>
+struct KvTraits<kKvF32> { static constexpr int bytes = 4; };
+template <>
+struct KvTraits<kKvBf16> { static constexpr int bytes = 2; };
+template <>
+struct KvTraits<kKvFp8> { static constexpr int bytes = 1; };
+
+// Load N consecutive cache elements (16-byte aligned, N*bytes a multiple of 16) as fp32.
+template <int KV, int N>
+__device__ __forceinline__ void load_elems(const uint8_t* p, float* out) {
+  constexpr int kVec = N * KvTraits<KV>::bytes / 16;
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const uint4 w = v[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (KV == kKvF32) {
+        out[i * 4 + j] = __uint_as_float(ws[j]);
+      } else if constexpr (KV == kKvBf16) {
+        out[i * 8 + 2 * j] = bf16_bits_to_f32(ws[j] & 0xffffu);
+        out[i * 8 + 2 * j + 1] = bf16_bits_to_f32(ws[j] >> 16);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[i * 16 + 4 * j + k] = e4m3_to_f32((ws[j] >> (8 * k)) & 0xffu);
+      }
+    }
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ float load_elem(const uint8_t* base, int64_t idx) {
+  if constexpr (KV == kKvF32) return reinterpret_cast<const float*>(base)[idx];
+  else if constexpr (KV == kKvBf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  else return e4m3_to_f32(base[idx]);
+}
+
+template <bool kQBf16>
+__device__ __forceinline__ float load_q(const void* q, int64_t idx) {
+  if constexpr (kQBf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q)[idx]);
+  else return reinterpret_cast<const float*>(q)[idx];
+}
+
+template <bool kQBf16>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (kQBf16) reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits_rne(v);
+  else reinterpret_cast<float*>(out)[idx] = v;
+}
+
+__device__ __forceinline__ int seq_context(const DecodeArgs& a, int b) {
+  int ctx = a.context_lens[b];
+  ctx = ctx < 0 ? 0 : ctx;
+  ctx = min(ctx, a.max_context_len);
+  return min(ctx, a.max_blocks_per_seq * kBlockTokens);
+}
+
+__device__ __forceinline__ int64_t phys_block(const DecodeArgs& a, int b, int logical) {
+  int blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + logical];
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  return blk;
+}
+
+template <bool kQBf16, int KV, int D>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int kDQ = D / 4;            // elements of a K row per lane (4 lanes per token)
+  constexpr int kEb = KvTraits<KV>::bytes;
+  __shared__ float q_s[kMaxGroup][D];
+  __shared__ float s_s[kMaxGroup][kMaxPartitionTokens];
+  __shared__ float m_s[kMaxGroup], l_s[kMaxGroup];
+
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int P = a.partition_tokens;
+  const int ctx = seq_context(a, b);
+  const int nparts = (ctx + P - 1) / P;
+  const int64_t head0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;   // first query head row
+
+  if (ctx == 0) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<kQBf16>(a.out, head0 * D + i, 0.0f);
+    return;
+  }
+  const int t0 = part * P;
+  if (t0 >= ctx) return;
+  const int n = min(P, ctx - t0);
+
+  for (int i = threadIdx.x; i < G * D; i += kThreads)
+    q_s[i / D][i % D] = load_q<kQBf16>(a.q, head0 * D + i) * a.scale_log2;
+  __syncthreads();
+
+  // Phase 1: scores.  Wave w takes blocks w, w+4, ...; lane -> (token lane/4, quarter lane%4).
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int tok = lane / 4, quarter = lane % 4;
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  for (int i = wave; i < nblk; i += 4) {
+    const int logical = t0 / kBlockTokens + i;
+    const int64_t phys = phys_block(a, b, logical);
+    const int64_t row = ((phys * a.num_kv_heads + g) * kBlockTokens + tok) * D + quarter * kDQ;
+    float kv[kDQ];
+    load_elems<KV, kDQ>(kbase + row * kEb, kv);
+    const float ks = (KV == kKvFp8) ? a.k_scale[phys * a.num_kv_heads + g] : 1.0f;
+    const int t = i * kBlockTokens + tok;   // token index inside the partition
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < kDQ; ++d) acc += q_s[h][quarter * kDQ + d] * kv[d];
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (quarter == 0) s_s[h][t] = (t < n) ? acc * ks : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: per-head max and sum over the partition's tokens.
+  for (int h = wave; h < G; h += 4) {
+    float m = -INFINITY;
+    for (int t = lane; t < n; t += 64) m = fmaxf(m, s_s[h][t]);
+    m = wave_max(m);
+    float l = 0.0f;
+    for (int t = lane; t < n; t += 64) {
+      const float e = exp2f(s_s[h][t] - m);
+      s_s[h][t] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    if (lane == 0) { m_s[h] = m; l_s[h] = l; }
+  }
+  __syncthreads();
+
+  // Phase 3: P.V.  Thread -> (column d, head slice hs); heads hs, hs+HS, ...
+  constexpr int kHS = kThreads / D;
+  constexpr int kMaxPer = kMaxGroup / kHS;
+  const int d = threadIdx.x % D, hs = threadIdx.x / D;
+  float acc[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) acc[j] = 0.0f;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  for (int i = 0; i < nblk; ++i) {
+    const int64_t phys = phys_block(a, b, t0 / kBlockTokens + i);
+    const float vs = (KV == kKvFp8) ? a.v_scale[phys * a.num_kv_heads + g] : 1.0f;
+    const int64_t base = (phys * a.num_kv_heads + g) * kBlockTokens * D + d;
+    const int tn = min(kBlockTokens, n - i * kBlockTokens);
+    for (int tt = 0; tt < tn; ++tt) {
+      const float v = load_elem<KV>(vbase, base + (int64_t)tt * D) * vs;
+      const int t = i * kBlockTokens + tt;
+#pragma unroll
+      for (int j = 0; j < kMaxPer; ++j) {
+        const int h = hs + j * kHS;
+        if (h < G) acc[j] += s_s[h][t] * v;
+      }
+    }
+  }
+
+  if (nparts == 1) {
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int h = hs + j * kHS;
+      if (h < G) store_out<kQBf16>(a.out, (head0 + h) * D + d, acc[j] / l_s[h]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int h = hs + j * kHS;
+      if (h < G) {
+        const int64_t r = (head0 + h) * a.num_parts + part;
+        a.ws_acc[r * D + d] = acc[j];
+        if (d == 0) { a.ws_m[r] = m_s[h]; a.ws_l[r] = l_s[h]; }
+      }
+    }
+  }
+}
+
+// Merge: one workgroup of D threads per (query head, sequence).
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+template <bool kQBf16, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int P = a.partition_tokens;
+  const int ctx = seq_context(a, b);
+  const int nparts = (ctx + P - 1) / P;
+  if (nparts <= 1) return;            // written by the partition kernel
+  const int64_t row = (int64_t)b * a.num_q_heads + h;
+  const float* m = a.ws_m + row * a.num_parts;
+  const float* l = a.ws_l + row * a.num_parts;
+  const float* acc = a.ws_acc + row * a.num_parts * D;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, m[p]);
+  float num = 0.0f, den = 0.0f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = exp2f(m[p] - M);
+    den += w * l[p];
+    num += w * acc[(int64_t)p * D + d];
+  }
+  store_out<kQBf16>(a.out, row * D + d, num / den);
+}
+
+template <bool kQBf16, int KV>
+hipError_t launch_valu(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((decode_valu_kernel<kQBf16, KV, 64>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<kQBf16, KV, 128>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
+  if (a.q_dtype == PA_DTYPE_F32) return launch_valu<false, kKvF32>(a, stream);
+  if (a.cache_dtype == PA_DTYPE_BF16) return launch_valu<true, kKvBf16>(a, stream);
+  return launch_valu<true, kKvFp8>(a, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.num_seqs);
+  const bool bf16 = a.q_dtype == PA_DTYPE_BF16;
+  if (a.head_dim == 64) {
+    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(128), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,286 @@
+// C-ABI layer of libpa: argument validation, dtype/shape dispatch, partition
+// choice, workspace layout, launches, status codes and the timing hooks.
+//
+// Validation happens entirely on the host and before any HIP call, so a
+// rejected call never touches the GPU.
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace pa {
+
+size_t align_floats(size_t n) { return (n + 63) / 64 * 64; }  // 256-byte sections
+
+size_t workspace_section_floats(int32_t num_seqs, int32_t num_q_heads, int32_t num_parts) {
+  return align_floats((size_t)num_seqs * num_q_heads * num_parts);
+}
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool valid_dtype(int d) { return d == PA_DTYPE_F32 || d == PA_DTYPE_BF16 || d == PA_DTYPE_FP8_E4M3; }
+
+// Automatic partition length: whole sequences when they are short, else
+// 512-token partitions (a multiple of the 16-token block).
+int32_t auto_partition(int32_t max_context_len) {
+  if (max_context_len <= kMaxPartitionTokens) {
+    const int32_t p = (max_context_len + 15) / 16 * 16;
+    return p < 16 ? 16 : p;
+  }
+  return kMaxPartitionTokens;
+}
+
+int check_decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs < 0 || num_seqs > 65535) return PA_ERR_BAD_SHAPE;
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_kv_heads > 65535) return PA_ERR_BAD_SHAPE;
+  if (num_q_heads % num_kv_heads) return PA_ERR_BAD_SHAPE;
+  if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (max_context_len < 0) return PA_ERR_BAD_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % 16 || partition_tokens > kMaxPartitionTokens)
+    return PA_ERR_BAD_SHAPE;
+  return PA_OK;
+}
+
+struct WorkspaceLayout {
+  int32_t partition_tokens = 0;
+  int32_t num_parts = 1;
+  size_t bytes = 0;
+  size_t m_off = 0, l_off = 0, acc_off = 0;  // in floats
+};
+
+WorkspaceLayout layout_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                           int32_t partition_tokens) {
+  WorkspaceLayout w;
+  w.partition_tokens = partition_tokens > 0 ? partition_tokens : auto_partition(max_context_len);
+  const int32_t parts = (max_context_len + w.partition_tokens - 1) / w.partition_tokens;
+  w.num_parts = parts < 1 ? 1 : parts;
+  if (w.num_parts <= 1) return w;
+  const size_t sec = workspace_section_floats(num_seqs, num_q_heads, w.num_parts);
+  w.m_off = 0;
+  w.l_off = sec;
+  w.acc_off = 2 * sec;
+  w.bytes = (2 * sec + align_floats((size_t)num_seqs * num_q_heads * w.num_parts * head_dim)) * sizeof(float);
+  return w;
+}
+
+// ---- timing hooks -----------------------------------------------------------
+
+struct TimingRecord {
+  hipEvent_t start, mid, end;
+  bool merged;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimingRecord> pool;
+  size_t used = 0;
+} g_timing;
+
+constexpr size_t kMaxTimedCalls = 65536;
+
+TimingRecord* timing_slot() {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (!g_timing.enabled || g_timing.used >= kMaxTimedCalls) return nullptr;
+  if (g_timing.used == g_timing.pool.size()) {
+    TimingRecord r{};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.mid) != hipSuccess ||
+        hipEventCreate(&r.end) != hipSuccess)
+      return nullptr;
+    g_timing.pool.push_back(r);
+  }
+  return &g_timing.pool[g_timing.used++];
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+PA_EXPORT const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "a size is negative, inconsistent or out of range";
+    case PA_ERR_BAD_DTYPE: return "unknown dtype or unsupported dtype combination";
+    case PA_ERR_UNSUPPORTED: return "head_dim or group size outside the supported set";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_MISALIGNED: return "a q/out/cache pointer is not 16-byte aligned";
+    case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+PA_EXPORT int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype, void* k_cache, void* v_cache,
+                             pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                             const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_BAD_SHAPE;
+  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  if (cache_dtype == PA_DTYPE_FP8_E4M3) {
+    if (src_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_BAD_DTYPE;
+  } else if (src_dtype != cache_dtype) {
+    return PA_ERR_BAD_DTYPE;
+  }
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
+  CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens, num_kv_heads,
+                   head_dim, num_blocks, src_dtype, cache_dtype};
+  return launch_cache_write(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+PA_EXPORT int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_context_len,
+                                             int32_t partition_tokens) {
+  const int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                    partition_tokens);
+  if (st != PA_OK) return st;
+  return layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).partition_tokens;
+}
+
+PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
+  if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens) !=
+      PA_OK)
+    return 0;
+  return layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).bytes;
+}
+
+PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* k_cache, const void* v_cache,
+                        pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens);
+  if (st != PA_OK) return st;
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  const bool combo_ok = (q_dtype == PA_DTYPE_F32 && cache_dtype == PA_DTYPE_F32) ||
+                        (q_dtype == PA_DTYPE_BF16 && cache_dtype == PA_DTYPE_BF16) ||
+                        (q_dtype == PA_DTYPE_BF16 && cache_dtype == PA_DTYPE_FP8_E4M3);
+  if (!combo_ok) return PA_ERR_BAD_DTYPE;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
+  const WorkspaceLayout w = layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
+  if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return PA_ERR_WORKSPACE;
+  if (w.bytes > 0 && !aligned16(workspace)) return PA_ERR_MISALIGNED;
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  float* ws = reinterpret_cast<float*>(workspace);
+  a.ws_m = w.bytes ? ws + w.m_off : nullptr;
+  a.ws_l = w.bytes ? ws + w.l_off : nullptr;
+  a.ws_acc = w.bytes ? ws + w.acc_off : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.partition_tokens = w.partition_tokens;
+  a.num_parts = w.num_parts;
+  a.scale_log2 = scale * kLog2e;
+  a.q_dtype = q_dtype;
+  a.cache_dtype = cache_dtype;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  TimingRecord* rec = timing_slot();
+  if (rec) (void)hipEventRecord(rec->start, s);
+  if (launch_decode_partitions(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (rec) (void)hipEventRecord(rec->mid, s);
+  if (w.num_parts > 1) {
+    if (launch_decode_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (rec) {
+    rec->merged = w.num_parts > 1;
+    (void)hipEventRecord(rec->end, s);
+  }
+  return PA_OK;
+}
+
+PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype, float* k_scale, float* v_scale,
+                             const int32_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t num_blocks, void* stream) {
+  if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_BAD_SHAPE;
+  if (!valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 256) return PA_ERR_BAD_SHAPE;   // scales are copied by one workgroup's lanes
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL_POINTER;
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
+  CopyBlocksArgs a{k_cache, v_cache, k_scale, v_scale, block_pairs, num_pairs, num_kv_heads, head_dim,
+                   num_blocks, cache_dtype};
+  return launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+PA_EXPORT int pa_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  g_timing.enabled = enable != 0;
+  return PA_OK;
+}
+
+PA_EXPORT int pa_timing_read(double* partition_ms, double* merge_ms, int64_t* calls) {
+  if (!partition_ms || !merge_ms || !calls) return PA_ERR_NULL_POINTER;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  double part = 0.0, merge = 0.0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    TimingRecord& r = g_timing.pool[i];
+    if (hipEventSynchronize(r.end) != hipSuccess) return PA_ERR_LAUNCH;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.start, r.mid) != hipSuccess) return PA_ERR_LAUNCH;
+    part += ms;
+    if (r.merged) {
+      if (hipEventElapsedTime(&ms, r.mid, r.end) != hipSuccess) return PA_ERR_LAUNCH;
+      merge += ms;
+    }
+  }
+  *partition_ms = part;
+  *merge_ms = merge;
+  *calls = (int64_t)g_timing.used;
+  g_timing.used = 0;
+  return PA_OK;
+}
+
+PA_EXPORT size_t pa_probe_sink_bytes(void) { return probe_sink_bytes(); }
+
+PA_EXPORT int pa_probe_stream_read(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return PA_ERR_NULL_POINTER;
+  if (bytes % 16) return PA_ERR_BAD_SHAPE;
+  if (!aligned16(buf) || !aligned16(sink)) return PA_ERR_MISALIGNED;
+  return launch_probe_stream_read(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_LAUNCH;
+}
+
+PA_EXPORT int pa_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return PA_ERR_NULL_POINTER;
+  if (bytes % 16) return PA_ERR_BAD_SHAPE;
+  if (!aligned16(dst) || !aligned16(src)) return PA_ERR_MISALIGNED;
+  return launch_probe_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                                  : PA_ERR_LAUNCH;
+}

@@ -1,0 +1,56 @@
+// Measurement probes: a plain 16-byte streaming read and a plain copy.
+// They give the bandwidth the memory system sustains for a simple stream,
+// the ceiling the decode kernels are compared with.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeBlocks = 256 * 16;   // 16 workgroups per CU on a 256-CU part
+
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* buf, int64_t n16, uint4* sink) {
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = buf[i];
+    acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+  }
+  // fold the workgroup's lanes so the loads stay live; one 16-byte word per workgroup
+  __shared__ uint4 red[kProbeThreads];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = kProbeThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      uint4 o = red[threadIdx.x + s];
+      red[threadIdx.x].x ^= o.x; red[threadIdx.x].y ^= o.y;
+      red[threadIdx.x].z ^= o.z; red[threadIdx.x].w ^= o.w;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(uint4* dst, const uint4* src, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+size_t probe_sink_bytes() { return (size_t)kProbeBlocks * 16; }
+
+hipError_t launch_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(buf), (int64_t)(bytes / 16), reinterpret_cast<uint4*>(sink));
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, stream,
+                     reinterpret_cast<uint4*>(dst), reinterpret_cast<const uint4*>(src), (int64_t)(bytes / 16));
+  return hipGetLastError();
+}
+
+}  // namespace pa
