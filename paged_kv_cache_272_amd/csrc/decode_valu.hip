@@ -240,6 +240,11 @@ hipError_t launch_valu(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_dtype == PA_DTYPE_F32) return launch_valu<false, kKvF32>(a, stream);
+  return launch_decode_mfma(a, stream);
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
+  if (a.q_dtype == PA_DTYPE_F32) return launch_valu<false, kKvF32>(a, stream);
   if (a.cache_dtype == PA_DTYPE_BF16) return launch_valu<true, kKvBf16>(a, stream);
   return launch_valu<true, kKvFp8>(a, stream);
 }

@@ -62,6 +62,9 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 // Writes `out` directly for sequences that fit one partition, partial
 // results into the workspace otherwise.
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+// Matrix-core partition kernel for a bf16 query (bf16 or e4m3 cache); the
+// generic VALU kernel serves the fp32 path.
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Merge kernel: combines the partial results of multi-partition sequences.
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
