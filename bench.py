@@ -142,13 +142,13 @@ def main():
     part = pa.pa_decode_partition_tokens(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                          wl.max_context_len, args.partition_tokens)
     ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                           wl.max_context_len, part)
+                                           wl.max_context_len, args.partition_tokens)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     steps = []
     for kc, vc in pools:
         steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
                       pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale,
-                                        partition_tokens=part, workspace=ws)))
+                                        partition_tokens=args.partition_tokens, workspace=ws)))
 
     import oracle
     decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
@@ -208,7 +208,9 @@ def main():
             "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim, "block_size": 16, "context_lens": "U{128..4096}",
             "sum_context": int(wl.context_lens.sum()), "kv_dtype": "bf16", "pool_blocks": wl.num_blocks,
-            "pools_rotated": len(pools), "partition_tokens": part,
+            "pools_rotated": len(pools),
+            "work_split": ("balanced slices of the (sequence, block) list" if args.partition_tokens == 0
+                           else f"{part}-token partitions"),
             "step": "pa_cache_write(64 tokens) + pa_decode",
         },
         "seqs_per_s": round(wl.num_seqs / step_s, 1),

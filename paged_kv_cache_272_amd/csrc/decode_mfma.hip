@@ -6,12 +6,9 @@
 // table (section 2.3), with the online-softmax tiling idea of section 3.2
 // (the running-max rescale that page omits is applied exactly).
 //
-// Work split.  One workgroup of 4 waves per (partition, KV head, sequence);
-// wave w takes the partition's 16-token blocks w, w+4, ... and keeps its
-// own running max / sum / output; the 4 waves merge through LDS at the end.
-// A single wave holds one K/V block in registers and applies it to all G
-// query heads of the GQA group at once: the heads are the N dimension of
-// the MFMAs, so each block is read from HBM exactly once per group.
+// One wave owns one KV head and applies each 16-token K/V block it loads to
+// all G query heads of that head's group at once: the query heads are the N
+// dimension of the MFMAs, so a block is read from HBM once per group.
 //
 // Per block (16 tokens), lane l = 16*c + r (r = l%16, c = l/16):
 //   QK:  S^T[token][head] = K[token][:] . Q[head][:]  with D/32 MFMAs
@@ -34,6 +31,10 @@
 // e4m3 codes are widened to bf16 exactly (every e4m3 value is a bf16
 // value); the per-(block, head) scales multiply the logits (K) and the
 // probabilities fed to P.V (V).
+//
+// Two work splits (see DecodeArgs): a partition grid, and a balanced split
+// in which every workgroup takes an equal slice of all (sequence, block)
+// units, so no compute unit idles at the end of the launch.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -45,8 +46,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kPartWaves = 4;
+constexpr int kPartThreads = 64 * kPartWaves;
 
 // All-reduce over the lane pairs (l, l^32) and (l, l^16): each permlane swap
 // returns, per lane, its own value and its partner's (in some order).
@@ -79,6 +80,15 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
+  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+
+__device__ __forceinline__ int clamp_context(const DecodeArgs& a, int b) {
+  const int ctx = a.context_lens[b];
+  return ctx < 0 ? 0 : min(min(ctx, a.max_context_len), a.max_blocks_per_seq * kBlockTokens);
+}
+
 template <int D, bool kFp8>
 struct Tile {
   static constexpr int kKSteps = D / 32;                  // QK MFMAs (16x16x32)
@@ -106,6 +116,7 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
   }
 }
 
+// One 16-token K/V block of one KV head, as this lane holds it.
 template <int D, bool kFp8>
 struct BlockRegs {
   uint32_t k[Tile<D, kFp8>::kKWords];
@@ -123,67 +134,34 @@ __device__ __forceinline__ void load_block(BlockRegs<D, kFp8>& br, const uint8_t
     load_words<T::kVWords>(vbase + ((head_base + 4 * c + e) * D + T::kE * r) * T::kEb, br.v[e]);
 }
 
+// Running state of one wave: G query heads of one KV head over a run of blocks.
 template <int D, bool kFp8>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
+struct HeadState {
   using T = Tile<D, kFp8>;
-  constexpr int kE = T::kE;
-  __shared__ float lds_m[kWaves][16];
-  __shared__ float lds_l[kWaves][16];
-  __shared__ f32x4_t lds_acc[kWaves][kE][64];
-
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, c = lane >> 4;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int P = a.partition_tokens;
-
-  int ctx = a.context_lens[b];
-  ctx = ctx < 0 ? 0 : min(min(ctx, a.max_context_len), a.max_blocks_per_seq * kBlockTokens);
-  const int nparts = (ctx + P - 1) / P;
-  const int64_t head0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  if (ctx == 0) {
-    if (part == 0)
-      for (int i = threadIdx.x; i < G * D; i += kThreads) out[head0 * D + i] = 0;
-    return;
-  }
-  const int t0 = part * P;
-  if (t0 >= ctx) return;
-  const int n = min(P, ctx - t0);
-  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
-  const int nw = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;   // blocks of this wave
-
-  // Q^T operand: head r (zero for r >= G), d chunk (D/32)*c + i.
+  static constexpr int kE = T::kE;
   bf16x8_t qop[T::kKSteps];
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (head0 + r) * D + (D / 4) * c;
+  f32x4_t acc[kE];
+  float m, l;
+
+  // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
+  __device__ __forceinline__ void begin(const uint16_t* q, int64_t q_row0, int G, int r, int c) {
+    const uint16_t* qp = q + (q_row0 + r) * D + (D / 4) * c;
 #pragma unroll
     for (int i = 0; i < T::kKSteps; ++i) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (r < G) w = reinterpret_cast<const uint4*>(q)[i];
+      if (r < G) w = reinterpret_cast<const uint4*>(qp)[i];
       qop[i] = __builtin_bit_cast(bf16x8_t, w);
     }
-  }
-  // physical ids (and fp8 scales) of this wave's blocks: lane j holds block j
-  int my_blk = 0;
-  float my_ks = 1.0f, my_vs = 1.0f;
-  if (lane < nw) {
-    int blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + t0 / kBlockTokens + wave + kWaves * lane];
-    my_blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    if constexpr (kFp8) {
-      my_ks = a.k_scale[(int64_t)my_blk * a.num_kv_heads + g];
-      my_vs = a.v_scale[(int64_t)my_blk * a.num_kv_heads + g];
-    }
-  }
-
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
-  float m = -INFINITY, l = 0.0f;
-  f32x4_t acc[kE];
+    m = -INFINITY;
+    l = 0.0f;
 #pragma unroll
-  for (int t = 0; t < kE; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < kE; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  auto compute = [&](const BlockRegs<D, kFp8>& br, int i) {
+  // Fold one block in.  `valid` = tokens of the block inside the context
+  // (1..16), `sc` = scale*log2(e) (times the block's K scale for e4m3),
+  // `vs` = the block's V scale.
+  __device__ __forceinline__ void step(const BlockRegs<D, kFp8>& br, int valid, float sc, float vs, int c) {
     // ---- S^T = K . Q^T
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -197,15 +175,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
       }
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
     }
-    float sc = a.scale_log2;
-    float vs = 1.0f;
-    if constexpr (kFp8) {
-      sc *= __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i));
-      vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i));
-    }
     float sv[4] = {s[0] * sc, s[1] * sc, s[2] * sc, s[3] * sc};
-    const int valid = n - (wave + kWaves * i) * kBlockTokens;   // tokens of this block inside the context
-    uint32_t vmask = 0xffffffffu;                                // per-token keep mask for V (bit e)
+    uint32_t vmask = 0xfu;                                        // tokens 4c+e kept for P.V (bit e)
     if (valid < kBlockTokens) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -231,7 +202,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
     l += (p[0] + p[1]) + (p[2] + p[3]);
     const short4_t pop = __builtin_bit_cast(
         short4_t, make_uint2(pack_bf16x2(p[0] * vs, p[1] * vs), pack_bf16x2(p[2] * vs, p[3] * vs)));
-    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n)
+    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n).  Masked
+    // tokens get V = 0 by selection (their slots may hold NaN).
     uint32_t vw[4][T::kVWords];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -257,6 +229,99 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
       const short4_t vop = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
       acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[nn], 0, 0, 0);
     }
+  }
+
+  // The wave's total sum (the 4 lane groups hold partial sums of one head).
+  __device__ __forceinline__ float total_l() const { return sum_xor16(sum_xor32(l)); }
+
+  // Output run of this lane: d = (D/4)*c + kE*j + n  ->  o[kE*j + n].
+  __device__ __forceinline__ void unpack(float* o) const {
+#pragma unroll
+    for (int nn = 0; nn < kE; ++nn)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[kE * j + nn] = acc[nn][j];
+  }
+};
+
+// Write D/4 normalised values of one query row as bf16 (16-byte stores).
+template <int D>
+__device__ __forceinline__ void store_bf16_run(uint16_t* dst_row, int d0, const float* o, float inv) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(dst_row + d0);
+#pragma unroll
+  for (int i = 0; i < D / 8; i += 4) {
+    const uint4 w = make_uint4(pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv),
+                               pack_bf16x2(o[2 * i + 2] * inv, o[2 * i + 3] * inv),
+                               pack_bf16x2(o[2 * i + 4] * inv, o[2 * i + 5] * inv),
+                               pack_bf16x2(o[2 * i + 6] * inv, o[2 * i + 7] * inv));
+    *reinterpret_cast<uint4*>(dst + i) = w;
+  }
+}
+
+// Write D/4 unnormalised fp32 values of one workspace row.
+template <int D>
+__device__ __forceinline__ void store_f32_run(float* dst_row, int d0, const float* o) {
+  float4* dst = reinterpret_cast<float4*>(dst_row + d0);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// Partition grid: one workgroup of 4 waves per (partition, KV head, sequence);
+// wave w takes the partition's blocks w, w+4, ... and the waves merge in LDS.
+
+template <int D, bool kFp8>
+__global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a) {
+  using T = Tile<D, kFp8>;
+  constexpr int kE = T::kE;
+  __shared__ float lds_m[kPartWaves][16];
+  __shared__ float lds_l[kPartWaves][16];
+  __shared__ f32x4_t lds_acc[kPartWaves][kE][64];
+
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int P = a.partition_tokens;
+
+  const int ctx = clamp_context(a, b);
+  const int nparts = (ctx + P - 1) / P;
+  const int64_t head0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  if (ctx == 0) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < G * D; i += kPartThreads) out[head0 * D + i] = 0;
+    return;
+  }
+  const int t0 = part * P;
+  if (t0 >= ctx) return;
+  const int n = min(P, ctx - t0);
+  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
+  const int nw = wave < nblk ? (nblk - wave + kPartWaves - 1) / kPartWaves : 0;   // blocks of this wave
+
+  HeadState<D, kFp8> hs;
+  hs.begin(reinterpret_cast<const uint16_t*>(a.q), head0, G, r, c);
+  // physical ids (and fp8 scales) of this wave's blocks: lane j holds block j
+  int my_blk = 0;
+  float my_ks = 1.0f, my_vs = 1.0f;
+  if (lane < nw) {
+    my_blk = clamp_block(
+        a.block_tables[(int64_t)b * a.max_blocks_per_seq + t0 / kBlockTokens + wave + kPartWaves * lane],
+        a.num_blocks);
+    if constexpr (kFp8) {
+      my_ks = a.k_scale[(int64_t)my_blk * a.num_kv_heads + g];
+      my_vs = a.v_scale[(int64_t)my_blk * a.num_kv_heads + g];
+    }
+  }
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  auto step = [&](const BlockRegs<D, kFp8>& br, int i) {
+    float sc = a.scale_log2, vs = 1.0f;
+    if constexpr (kFp8) {
+      sc *= __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i));
+      vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i));
+    }
+    const int valid = min(kBlockTokens, n - (wave + kPartWaves * i) * kBlockTokens);
+    hs.step(br, valid, sc, vs, c);
   };
 
   // software pipeline: the next block's loads are in flight while this one computes
@@ -265,43 +330,43 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
   for (int i = 0; i < nw; i += 2) {
     if (i + 1 < nw)
       load_block<D, kFp8>(b1, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 1), a.num_kv_heads, g, r, c);
-    compute(b0, i);
+    step(b0, i);
     if (i + 1 < nw) {
       if (i + 2 < nw)
         load_block<D, kFp8>(b0, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 2), a.num_kv_heads, g, r, c);
-      compute(b1, i + 1);
+      step(b1, i + 1);
     }
   }
 
   // ---- wave totals, then the 4-wave merge through LDS
-  l = sum_xor16(sum_xor32(l));
+  const float lw = hs.total_l();
   if (c == 0) {
-    lds_m[wave][r] = m;
-    lds_l[wave][r] = l;
+    lds_m[wave][r] = hs.m;
+    lds_l[wave][r] = lw;
   }
 #pragma unroll
-  for (int t = 0; t < kE; ++t) lds_acc[wave][t][lane] = acc[t];
+  for (int t = 0; t < kE; ++t) lds_acc[wave][t][lane] = hs.acc[t];
   __syncthreads();
   if (wave != 0) return;
 
-  float mw[kWaves], M = -INFINITY;
+  float mw[kPartWaves], M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < kPartWaves; ++w) {
     mw[w] = lds_m[w][r];
     M = fmaxf(M, mw[w]);
   }
-  float L = 0.0f, wt[kWaves];
+  float L = 0.0f, wt[kPartWaves];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < kPartWaves; ++w) {
     wt[w] = __builtin_amdgcn_exp2f(mw[w] - M);   // waves without blocks have m = -inf -> 0
     L += wt[w] * lds_l[w][r];
   }
-  float o[4 * kE];   // d = (D/4)*c + kE*j + nn  ->  o[kE*j + nn]
+  float o[4 * kE];
 #pragma unroll
   for (int nn = 0; nn < kE; ++nn) {
     f32x4_t v = lds_acc[0][nn][lane] * wt[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += lds_acc[w][nn][lane] * wt[w];
+    for (int w = 1; w < kPartWaves; ++w) v += lds_acc[w][nn][lane] * wt[w];
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[kE * j + nn] = v[j];
   }
@@ -309,26 +374,222 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
   const int64_t row = head0 + r;
   const int d0 = (D / 4) * c;
   if (nparts == 1) {
-    const float inv = 1.0f / L;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(out + row * D + d0);
-#pragma unroll
-    for (int i = 0; i < 2 * kE; i += 4) {
-      uint4 w = make_uint4(pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv),
-                           pack_bf16x2(o[2 * i + 2] * inv, o[2 * i + 3] * inv),
-                           pack_bf16x2(o[2 * i + 4] * inv, o[2 * i + 5] * inv),
-                           pack_bf16x2(o[2 * i + 6] * inv, o[2 * i + 7] * inv));
-      *reinterpret_cast<uint4*>(dst + i) = w;
-    }
+    store_bf16_run<D>(out + row * D, d0, o, 1.0f / L);
   } else {
     const int64_t wr = row * a.num_parts + part;
-    float4* dst = reinterpret_cast<float4*>(a.ws_acc + wr * D + d0);
-#pragma unroll
-    for (int i = 0; i < kE; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    store_f32_run<D>(a.ws_acc + wr * D, d0, o);
     if (c == 0) {
       a.ws_m[wr] = M;
       a.ws_l[wr] = L;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split.  Units are (sequence, 16-token block) pairs laid end to end
+// in sequence order; sequence b owns units [start[b], start[b+1]).  Workgroup
+// x takes units [x*per, (x+1)*per), per = ceil(U / num_wgs); wave w of
+// workgroup (x, y) handles KV head y*waves + w over that slice.
+
+struct UnitIds {
+  int b, i, blk;       // lane j: the (sequence, logical block, physical block) of unit base + j
+  float ks, vs;        // fp8 block scales of that unit for this wave's head
+};
+
+__device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int u) {
+  // largest b with start[b] <= u (start is non-decreasing; start[num_seqs] > u)
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int g,
+                                            int lane) {
+  UnitIds id{0, 0, 0, 1.0f, 1.0f};
+  const int u = base + lane;
+  if (u < u1) {
+    id.b = find_sequence(start, a.num_seqs, u);
+    id.i = u - start[id.b];
+    id.blk = clamp_block(a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i], a.num_blocks);
+    if constexpr (kFp8) {
+      id.ks = a.k_scale[(int64_t)id.blk * a.num_kv_heads + g];
+      id.vs = a.v_scale[(int64_t)id.blk * a.num_kv_heads + g];
+    }
+  }
+  return id;
+}
+
+template <int D, bool kFp8>
+struct Pending {
+  BlockRegs<D, kFp8> regs;
+  int b, i;
+  float ks, vs;
+};
+
+template <int D, bool kFp8>
+__global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_kernel(DecodeArgs a) {
+  constexpr int kE = Tile<D, kFp8>::kE;
+  extern __shared__ int s_dyn[];                 // start[B + 1], then ctx[B]
+  __shared__ int s_wave_tot[kBalancedMaxWaves];
+  int* s_start = s_dyn;
+  int* s_ctx = s_dyn + a.num_seqs + 1;
+
+  const int x = blockIdx.x, y = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int W = a.waves_per_wg;
+  const int B = a.num_seqs;
+  const int G = a.num_q_heads / a.num_kv_heads;
+
+  // ---- unit prefix over the sequences (every workgroup computes it)
+  int carry = 0;
+  for (int base = 0; base < B; base += W * 64) {
+    const int b = base + tid;
+    int nb = 0;
+    if (b < B) {
+      const int ctx = clamp_context(a, b);
+      s_ctx[b] = ctx;
+      nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+    }
+    int v = nb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) s_wave_tot[wave] = v;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < W; ++w) {
+      const int t = s_wave_tot[w];
+      before += (w < wave) ? t : 0;
+      total += t;
+    }
+    if (b < B) s_start[b] = carry + before + v - nb;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) s_start[B] = carry;
+  __syncthreads();
+  const int U = carry;
+  const int per = (U + a.num_wgs - 1) / a.num_wgs;
+  const int u0 = min(U, x * per), u1 = min(U, u0 + per);
+  if (x == 0 && y == 0)
+    for (int b = tid; b <= B; b += W * 64) a.ws_seq_start[b] = s_start[b];
+
+  const int g = y * W + wave;
+  if (g >= a.num_kv_heads) return;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  // empty sequences own no unit: workgroup 0 writes their zero rows
+  if (x == 0) {
+    for (int b = 0; b < B; ++b)
+      if (s_ctx[b] == 0)
+        for (int i = lane; i < G * D; i += 64) out[((int64_t)b * a.num_q_heads + (int64_t)g * G) * D + i] = 0;
+  }
+  if (u0 >= u1) return;
+
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  const int d0 = (D / 4) * c;
+
+  HeadState<D, kFp8> hs;
+  int cur_b = -1;
+  auto finish = [&](int b) {
+    const float L = hs.total_l();
+    float o[4 * kE];
+    hs.unpack(o);
+    if (r >= G) return;
+    const int64_t row = (int64_t)b * a.num_q_heads + (int64_t)g * G + r;
+    const bool whole = s_start[b] >= u0 && s_start[b + 1] <= u1;
+    if (whole) {
+      store_bf16_run<D>(out + row * D, d0, o, 1.0f / L);
+    } else {
+      const int slot = s_start[b] < u0 ? 0 : 1;
+      const int64_t wr = ((int64_t)x * 2 + slot) * a.num_q_heads + (int64_t)g * G + r;
+      store_f32_run<D>(a.ws_acc + wr * D, d0, o);
+      if (c == 0) {
+        a.ws_m[wr] = hs.m;
+        a.ws_l[wr] = L;
+      }
+    }
+  };
+
+  // ids of the current 64-unit chunk and of the next one (kept one chunk ahead)
+  int base = u0;
+  UnitIds cur = unit_ids<kFp8>(a, s_start, base, u1, g, lane);
+  UnitIds nxt = unit_ids<kFp8>(a, s_start, base + 64, u1, g, lane);
+  auto fetch = [&](Pending<D, kFp8>& p, int u) {
+    if (u - base >= 64) {
+      base += 64;
+      cur = nxt;
+      nxt = unit_ids<kFp8>(a, s_start, base + 64, u1, g, lane);
+    }
+    const int j = u - base;
+    p.b = __builtin_amdgcn_readlane(cur.b, j);
+    p.i = __builtin_amdgcn_readlane(cur.i, j);
+    if constexpr (kFp8) {
+      p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
+      p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
+    } else {
+      p.ks = p.vs = 1.0f;
+    }
+    load_block<D, kFp8>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(cur.blk, j), a.num_kv_heads, g, r, c);
+  };
+  auto consume = [&](const Pending<D, kFp8>& p) {
+    if (p.b != cur_b) {
+      if (cur_b >= 0) finish(cur_b);
+      cur_b = p.b;
+      hs.begin(q, (int64_t)p.b * a.num_q_heads + (int64_t)g * G, G, r, c);
+    }
+    const int valid = min(kBlockTokens, s_ctx[p.b] - p.i * kBlockTokens);
+    hs.step(p.regs, valid, a.scale_log2 * p.ks, p.vs, c);
+  };
+
+  Pending<D, kFp8> p0, p1;
+  fetch(p0, u0);
+  for (int u = u0; u < u1; u += 2) {
+    if (u + 1 < u1) fetch(p1, u + 1);
+    consume(p0);
+    if (u + 1 < u1) {
+      if (u + 2 < u1) fetch(p0, u + 2);
+      consume(p1);
+    }
+  }
+  finish(cur_b);
+}
+
+// Merge for the balanced split: one workgroup of D threads per (query head,
+// sequence).  Sequence b's units are covered by workgroups w_first..w_last;
+// its partial sits in slot 1 of w_first (it began inside that slice) and in
+// slot 0 of every later one.
+//   out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_balanced_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int U = a.ws_seq_start[a.num_seqs];
+  const int per = (U + a.num_wgs - 1) / a.num_wgs;
+  const int s = a.ws_seq_start[b], e = a.ws_seq_start[b + 1];
+  if (s == e) return;
+  const int wf = s / per, wl = (e - 1) / per;
+  if (wf == wl) return;               // written whole by its workgroup
+  auto row = [&](int w) { return ((int64_t)w * 2 + (w == wf ? 1 : 0)) * a.num_q_heads + h; };
+  float M = -INFINITY;
+  for (int w = wf; w <= wl; ++w) M = fmaxf(M, a.ws_m[row(w)]);
+  float num = 0.0f, den = 0.0f;
+  for (int w = wf; w <= wl; ++w) {
+    const int64_t rw = row(w);
+    const float wt = __builtin_amdgcn_exp2f(a.ws_m[rw] - M);
+    den += wt * a.ws_l[rw];
+    num += wt * a.ws_acc[rw * D + d];
+  }
+  reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.num_q_heads + h) * D + d] =
+      (uint16_t)f32_to_bf16_bits_rne(num / den);
 }
 
 }  // namespace
@@ -337,12 +598,36 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
   if (a.head_dim == 128) {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, dim3(kPartThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, dim3(kPartThreads), 0, stream, a);
   } else {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, dim3(kPartThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, dim3(kPartThreads), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_balanced(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_wgs, a.head_groups);
+  const dim3 block(64 * a.waves_per_wg);
+  const size_t lds = (2 * (size_t)a.num_seqs + 1) * sizeof(int);
+  const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
+  if (a.head_dim == 128) {
+    if (fp8) hipLaunchKernelGGL((decode_mfma_balanced_kernel<128, true>), grid, block, lds, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<128, false>), grid, block, lds, stream, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((decode_mfma_balanced_kernel<64, true>), grid, block, lds, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<64, false>), grid, block, lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge_balanced(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.num_seqs);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_balanced_kernel<128>), grid, dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge_balanced_kernel<64>), grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -51,14 +51,17 @@ int check_decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 }
 
 struct WorkspaceLayout {
+  bool balanced = false;
   int32_t partition_tokens = 0;
   int32_t num_parts = 1;
+  int32_t num_wgs = 0, waves_per_wg = 0, head_groups = 0;
   size_t bytes = 0;
-  size_t m_off = 0, l_off = 0, acc_off = 0;  // in floats
+  size_t m_off = 0, l_off = 0, acc_off = 0, start_off = 0;  // in 4-byte words
 };
 
-WorkspaceLayout layout_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                           int32_t partition_tokens) {
+// Partition grid: partial rows (sequence, query head, partition).
+WorkspaceLayout partition_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens) {
   WorkspaceLayout w;
   w.partition_tokens = partition_tokens > 0 ? partition_tokens : auto_partition(max_context_len);
   const int32_t parts = (max_context_len + w.partition_tokens - 1) / w.partition_tokens;
@@ -70,6 +73,29 @@ WorkspaceLayout layout_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_d
   w.acc_off = 2 * sec;
   w.bytes = (2 * sec + align_floats((size_t)num_seqs * num_q_heads * w.num_parts * head_dim)) * sizeof(float);
   return w;
+}
+
+// Balanced split: partial rows (workgroup, slot 0/1, query head), plus the
+// per-sequence unit starts.  One wave per KV head, at most 8 waves per
+// workgroup, about kBalancedTargetWaves waves over the device.
+WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  WorkspaceLayout w;
+  w.balanced = true;
+  w.waves_per_wg = num_kv_heads < kBalancedMaxWaves ? num_kv_heads : kBalancedMaxWaves;
+  w.head_groups = (num_kv_heads + w.waves_per_wg - 1) / w.waves_per_wg;
+  const int32_t wgs = kBalancedTargetWaves / (w.waves_per_wg * w.head_groups);
+  w.num_wgs = wgs < 1 ? 1 : wgs;
+  const size_t rows = (size_t)w.num_wgs * 2 * num_q_heads;
+  w.m_off = 0;
+  w.l_off = align_floats(rows);
+  w.acc_off = 2 * align_floats(rows);
+  w.start_off = w.acc_off + align_floats(rows * head_dim);
+  w.bytes = (w.start_off + align_floats((size_t)num_seqs + 1)) * sizeof(float);
+  return w;
+}
+
+bool use_balanced(pa_dtype q_dtype, int32_t num_seqs, int32_t partition_tokens) {
+  return partition_tokens == 0 && q_dtype == PA_DTYPE_BF16 && num_seqs <= kBalancedMaxSeqs;
 }
 
 // ---- timing hooks -----------------------------------------------------------
@@ -147,7 +173,7 @@ PA_EXPORT int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_hea
   const int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                     partition_tokens);
   if (st != PA_OK) return st;
-  return layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).partition_tokens;
+  return partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).partition_tokens;
 }
 
 PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -155,7 +181,14 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens) !=
       PA_OK)
     return 0;
-  return layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).bytes;
+  // the automatic choice depends on the query type, which this query does not
+  // take: report enough for either split
+  size_t bytes = partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).bytes;
+  if (use_balanced(PA_DTYPE_BF16, num_seqs, partition_tokens)) {
+    const size_t b2 = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).bytes;
+    bytes = b2 > bytes ? b2 : bytes;
+  }
+  return bytes;
 }
 
 PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* k_cache, const void* v_cache,
@@ -177,7 +210,10 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
   if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
-  const WorkspaceLayout w = layout_for(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
+  const WorkspaceLayout w = use_balanced(q_dtype, num_seqs, partition_tokens)
+                                ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim)
+                                : partition_layout(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                   partition_tokens);
   if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return PA_ERR_WORKSPACE;
   if (w.bytes > 0 && !aligned16(workspace)) return PA_ERR_MISALIGNED;
 
@@ -194,6 +230,7 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   a.ws_m = w.bytes ? ws + w.m_off : nullptr;
   a.ws_l = w.bytes ? ws + w.l_off : nullptr;
   a.ws_acc = w.bytes ? ws + w.acc_off : nullptr;
+  a.ws_seq_start = w.balanced ? reinterpret_cast<int32_t*>(ws + w.start_off) : nullptr;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.num_seqs = num_seqs;
@@ -203,6 +240,10 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   a.num_blocks = num_blocks;
   a.partition_tokens = w.partition_tokens;
   a.num_parts = w.num_parts;
+  a.balanced = w.balanced ? 1 : 0;
+  a.num_wgs = w.num_wgs;
+  a.waves_per_wg = w.waves_per_wg;
+  a.head_groups = w.head_groups;
   a.scale_log2 = scale * kLog2e;
   a.q_dtype = q_dtype;
   a.cache_dtype = cache_dtype;
@@ -210,13 +251,16 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   TimingRecord* rec = timing_slot();
   if (rec) (void)hipEventRecord(rec->start, s);
-  if (launch_decode_partitions(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  const hipError_t e1 = w.balanced ? launch_decode_mfma_balanced(a, s) : launch_decode_partitions(a, s);
+  if (e1 != hipSuccess) return PA_ERR_LAUNCH;
   if (rec) (void)hipEventRecord(rec->mid, s);
-  if (w.num_parts > 1) {
-    if (launch_decode_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  const bool merge = w.balanced || w.num_parts > 1;
+  if (merge) {
+    const hipError_t e2 = w.balanced ? launch_decode_merge_balanced(a, s) : launch_decode_merge(a, s);
+    if (e2 != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (rec) {
-    rec->merged = w.num_parts > 1;
+    rec->merged = merge;
     (void)hipEventRecord(rec->end, s);
   }
   return PA_OK;

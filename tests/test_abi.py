@@ -91,7 +91,10 @@ def test_decode_validation(kw, status):
 
 
 def test_workspace_size_and_partition_queries():
-    assert lib_mod.pa_decode_workspace_size(64, 32, 8, 128, 512, 0) == 0
+    # one partition of 512 tokens holds every sequence: no scratch
+    assert lib_mod.pa_decode_workspace_size(64, 32, 8, 128, 512, 512) == 0
+    # the automatic (balanced) split always keeps partial rows and sequence starts
+    assert lib_mod.pa_decode_workspace_size(64, 32, 8, 128, 512, 0) > 0
     p = lib_mod.pa_decode_partition_tokens(64, 32, 8, 128, 4096, 0)
     assert p % 16 == 0 and 16 <= p
     assert lib_mod.pa_decode_partition_tokens(64, 32, 8, 128, 4096, 256) == 256

@@ -137,6 +137,40 @@ def test_partition_size_invariance(kv):
         assert err <= TOL[kv]
 
 
+@pytest.mark.parametrize("hq,hkv,d,kv", [(32, 8, 128, "bf16"), (64, 16, 128, "bf16"), (8, 1, 64, "bf16"),
+                                         (64, 8, 128, "fp8")])
+def test_many_short_sequences(hq, hkv, d, kv):
+    """Balanced split edges: slices holding many whole sequences, sequences cut by
+    slice edges, and more sequences than one scan pass covers."""
+    rng = np.random.default_rng(105)
+    lens = rng.integers(1, 60, size=1100)
+    lens[::37] = rng.integers(300, 900, size=len(lens[::37]))
+    wl = W.make_workload(name="short", seed=106, context_lens=lens, num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, q_dtype="bf16", kv_dtype=kv, fp8_mode="values")
+    if kv == "fp8":
+        quantize_fp8_values(wl)
+    _full_parity(wl, 40, False)
+
+
+def test_empty_sequences_between_live_ones():
+    wl = W.make_workload(name="gaps", seed=107, context_lens=[300, 5, 700, 64, 1, 2000, 33, 16], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    lens = wl.context_lens.copy()
+    lens[[1, 4, 7]] = 0
+    out = torch.full_like(dw.q, float("nan"))
+    pa.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, to_dev(lens, "i32"), wl.max_context_len,
+                 wl.scale)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    assert (got[[1, 4, 7]] == 0).all()
+    live = [0, 2, 3, 5, 6]
+    want = oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, lens, wl.scale, "bf16", "bf16", seqs=live)
+    assert np.abs(got[live] - want).max() <= TOL["bf16"]
+
+
 def test_zero_length_sequence_gives_zeros():
     wl = W.make_workload(name="zero", seed=103, context_lens=[5, 40], num_q_heads=8, num_kv_heads=2,
                          head_dim=64, q_dtype="bf16", kv_dtype="bf16")
