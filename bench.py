@@ -46,6 +46,9 @@ def kernel_source_hash() -> str:
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) into the "
+                         "HBM-traffic record the roofline entry reports, and exit")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -71,6 +74,65 @@ def measured_stream_read(pa, torch, nbytes=4 << 30, reps=5):
         best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del buf
     return best
+
+
+COPY_PROBE_BYTES = 1 << 30
+DECODE_KERNEL = "decode_mfma_balanced_kernel"
+COPY_KERNEL = "probe_copy_kernel"
+
+
+def copy_probe(pa, torch):
+    """One plain copy of known size: the calibration point for the HBM byte counters."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    pa.pa_probe_copy(dst, src)
+    torch.cuda.synchronize()
+
+
+def _counter_per_dispatch(run_dir, counter):
+    """{kernel-name substring: [per-dispatch value in bytes]} from a rocprofv3 counter CSV."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(path)):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row.get("Kernel_Name", "")
+            # FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch
+            out.setdefault(name, []).append(float(row["Counter_Value"]) * 1024.0)
+    return out
+
+
+def traffic_record(fetch_dir, write_dir):
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        vals = [v for name, vs in table.items() if key in name for v in vs]
+        if not vals:
+            raise SystemExit(f"no {key} dispatches in the counter output")
+        vals.sort()
+        return vals[len(vals) // 2]
+
+    copy_read, copy_write = pick(fetch, COPY_KERNEL), pick(write, COPY_KERNEL)
+    read_scale = COPY_PROBE_BYTES / copy_read
+    write_scale = COPY_PROBE_BYTES / copy_write
+    dec_read, dec_write = pick(fetch, DECODE_KERNEL), pick(write, DECODE_KERNEL)
+    rec = {
+        "kernel": DECODE_KERNEL,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_bytes_per_launch_raw": dec_read, "write_bytes_per_launch_raw": dec_write,
+        "copy_probe_bytes": COPY_PROBE_BYTES, "copy_probe_fetch_raw": copy_read, "copy_probe_write_raw": copy_write,
+        "read_scale": read_scale, "write_scale": write_scale,
+        "hbm_bytes_per_launch": round(dec_read * read_scale + dec_write * write_scale),
+        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (separate runs) over bench.py; median "
+                  "per-dispatch value, each scaled by (known bytes / counter) of a 1 GiB probe copy in the "
+                  "same run",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(wl, k_ref, v_ref, budget_s):
@@ -108,6 +170,9 @@ def cpu_baseline(wl, k_ref, v_ref, budget_s):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        traffic_record(*args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -143,7 +208,7 @@ def main():
                                          wl.max_context_len, args.partition_tokens)
     ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                            wl.max_context_len, args.partition_tokens)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     steps = []
     for kc, vc in pools:
         steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
@@ -156,6 +221,7 @@ def main():
     write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * 2 * 2 * 2 + wl.num_seqs * 8
     step_bytes = decode_bytes + write_bytes
 
+    copy_probe(pa, torch)
     peak_meas = measured_stream_read(pa, torch)
     print(f"# measured stream read {peak_meas:.0f} GB/s", file=sys.stderr, flush=True)
 

@@ -131,8 +131,9 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
               partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """out, q [B, Hq, D]; caches [NB, Hkv, 16, D]; block_tables [B, MB] int32; context_lens [B] int32.
 
-    If the call needs scratch and ``workspace`` is None, a byte tensor of
-    pa_decode_workspace_size() bytes is allocated on q's device.
+    If the call needs scratch and ``workspace`` is None, a zero-filled byte
+    tensor of pa_decode_workspace_size() bytes is allocated on q's device (a
+    caller-provided workspace must be zero-filled before its first use).
     """
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
@@ -143,7 +144,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     mb = block_tables.shape[1]
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
                           dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
@@ -220,7 +221,7 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_con
     num_blocks, hkv, _, _ = k_cache.shape
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),

@@ -1,7 +1,8 @@
 """Build libpa.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
 Every call compiles from source; the result lands next to this file so it
-travels with the source tree.
+travels with the source tree.  This script is loaded by file path (it must
+work before libpa.so exists, when the package itself cannot be imported).
 """
 from __future__ import annotations
 
@@ -45,10 +46,31 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_device_isa(src: str) -> None:
+    """Reject generated code that writes through the scalar data cache (the
+    opcode list and the scan live in isa_check.py, a build-time-only file)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("pa_isa_check", os.path.join(HERE, "isa_check.py"))
+    isa_check = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(isa_check)
+    asm = os.path.join(BUILD_DIR, os.path.basename(src) + ".s")
+    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"device assembly failed for {src}:\n{res.stderr}")
+    bad = isa_check.scalar_cache_writes(open(asm).read())
+    if bad:
+        raise RuntimeError(f"{src}: generated code writes through the scalar cache: {bad[0]}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(8, 2 * len(SOURCES))) as ex:
+        objs_f = [ex.submit(_compile, src) for src in SOURCES]
+        checks = [ex.submit(_check_device_isa, src) for src in SOURCES]
+        objs = [f.result() for f in objs_f]
+        for f in checks:
+            f.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -564,32 +564,65 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
   finish(cur_b);
 }
 
-// Merge for the balanced split: one workgroup of D threads per (query head,
-// sequence).  Sequence b's units are covered by workgroups w_first..w_last;
-// its partial sits in slot 1 of w_first (it began inside that slice) and in
-// slot 0 of every later one.
-//   out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w.
+// Merge for the balanced split.  Sequence b's units are covered by slices
+// w_first..w_last; its partial sits in slot 1 of w_first (it began inside
+// that slice) and in slot 0 of every later one.
+//   out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w,
+// taken in one pass with a running maximum, four partials per round so their
+// loads are in flight together.  Grid (sequence, chunk group): each thread
+// owns one 4-wide chunk of one query head's output row.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_balanced_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_balanced_kernel(DecodeArgs a) {
+  constexpr int kChunks = D / 4;                       // float4 chunks per output row
+  const int b = blockIdx.x;
+  const int it = blockIdx.y * kMergeThreads + threadIdx.x;
+  if (it >= a.num_q_heads * kChunks) return;
   const int U = a.ws_seq_start[a.num_seqs];
-  const int per = (U + a.num_wgs - 1) / a.num_wgs;
   const int s = a.ws_seq_start[b], e = a.ws_seq_start[b + 1];
-  if (s == e) return;
+  if (s == e) return;                                  // empty: zero row written by the decode kernel
+  const int per = (U + a.num_wgs - 1) / a.num_wgs;
   const int wf = s / per, wl = (e - 1) / per;
-  if (wf == wl) return;               // written whole by its workgroup
-  auto row = [&](int w) { return ((int64_t)w * 2 + (w == wf ? 1 : 0)) * a.num_q_heads + h; };
-  float M = -INFINITY;
-  for (int w = wf; w <= wl; ++w) M = fmaxf(M, a.ws_m[row(w)]);
-  float num = 0.0f, den = 0.0f;
-  for (int w = wf; w <= wl; ++w) {
-    const int64_t rw = row(w);
-    const float wt = __builtin_amdgcn_exp2f(a.ws_m[rw] - M);
-    den += wt * a.ws_l[rw];
-    num += wt * a.ws_acc[rw * D + d];
+  if (wf == wl) return;                                // written whole by its slice
+  const int n = wl - wf + 1;
+  const int h = it / kChunks, ch = it % kChunks;
+  float M = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int w0 = 0; w0 < n; w0 += 4) {
+    float mv[4], lv[4];
+    float4 av[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int w = wf + w0 + k;
+      if (w0 + k < n) {
+        const int64_t row = ((int64_t)w * 2 + (w == wf ? 1 : 0)) * a.num_q_heads + h;
+        mv[k] = a.ws_m[row];
+        lv[k] = a.ws_l[row];
+        av[k] = reinterpret_cast<const float4*>(a.ws_acc + row * D)[ch];
+      } else {
+        mv[k] = -INFINITY;
+        lv[k] = 0.0f;
+        av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+    const float Mn = fmaxf(M, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    const float sc = __builtin_amdgcn_exp2f(M - Mn);          // 0 while M is still -inf
+    den *= sc;
+    num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float wt = __builtin_amdgcn_exp2f(mv[k] - Mn);    // 0 for the padding entries
+      den += wt * lv[k];
+      num.x += wt * av[k].x; num.y += wt * av[k].y; num.z += wt * av[k].z; num.w += wt * av[k].w;
+    }
+    M = Mn;
   }
-  reinterpret_cast<uint16_t*>(a.out)[((int64_t)b * a.num_q_heads + h) * D + d] =
-      (uint16_t)f32_to_bf16_bits_rne(num / den);
+  const float inv = 1.0f / den;
+  const uint2 packed = make_uint2(f32_to_bf16_bits_rne(num.x * inv) | (f32_to_bf16_bits_rne(num.y * inv) << 16),
+                                  f32_to_bf16_bits_rne(num.z * inv) | (f32_to_bf16_bits_rne(num.w * inv) << 16));
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.num_q_heads + h) * D + 4 * ch) =
+      packed;
 }
 
 }  // namespace
@@ -623,11 +656,11 @@ hipError_t launch_decode_mfma_balanced(const DecodeArgs& a, hipStream_t stream) 
 }
 
 hipError_t launch_decode_merge_balanced(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_q_heads, a.num_seqs);
+  const dim3 grid(a.num_seqs, (a.num_q_heads * (a.head_dim / 4) + kMergeThreads - 1) / kMergeThreads);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL((decode_merge_balanced_kernel<128>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_balanced_kernel<128>), grid, dim3(kMergeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_merge_balanced_kernel<64>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_balanced_kernel<64>), grid, dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/pa.h"
+#include "pa.h"
 
 namespace pa {
 

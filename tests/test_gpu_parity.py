@@ -187,6 +187,34 @@ def test_zero_length_sequence_gives_zeros():
     assert np.abs(out_to_f64(out)[1] - want[0]).max() <= TOL["bf16"]
 
 
+def test_workspace_reused_across_calls():
+    """The in-kernel merge counters return to zero: one workspace serves many calls
+    and batches of different shapes."""
+    wl = W.make_workload(name="reuse", seed=108, context_lens=[3000, 100, 2048, 900, 17], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    want = oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16")
+    need = pa.pa_decode_workspace_size(5, 32, 8, 128, wl.max_context_len, 0)
+    ws = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    first = None
+    for it in range(4):
+        out = torch.empty_like(dw.q)
+        pa.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, wl.max_context_len,
+                     wl.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.abs(out_to_f64(out) - want).max() <= TOL["bf16"]
+        first = out.clone() if first is None else first
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16))
+        # a smaller batch through the same workspace in between
+        sub = torch.empty_like(dw.q[:2])
+        pa.pa_decode(sub, dw.q[:2].contiguous(), dw.k_cache, dw.v_cache, dw.block_tables[:2].contiguous(),
+                     dw.context_lens[:2].contiguous(), wl.max_context_len, wl.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.abs(out_to_f64(sub) - want[:2]).max() <= TOL["bf16"]
+
+
 def test_bitwise_repeatable():
     wl = W.make_workload(name="repeat", seed=104, context_lens=[3000, 100, 2048], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
