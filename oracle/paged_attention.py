@@ -27,6 +27,17 @@ What it computes, and where that is stated:
 * fp8 KV: codes times one float scale per (block, KV head); the scale is
   applied to the decoded code values before attention.
 
+Several new query tokens per sequence (``multi_query_ref``): a chunk of a
+chunked prefill ("17 · 连续批处理与 PagedAttention", section 二, remedy ①:
+a long prefill cut into pieces spread over iterations), the K draft tokens a
+target model checks in one pass ("推理优化", section 一, speculative
+decoding), or the unique suffix after a prefix-cache hit (same section,
+prefix caching).  The new tokens are the last ``q_len`` positions of the
+sequence and their K/V are already in the cache; token i of the chunk sits
+at position ``ctx - q_len + i`` and attends to every token at or before that
+position (the causal mask of "系统级优化…" section 3.3, aligned so that the
+last query token sees the whole context).
+
 Partitioned decode (``decode_partitioned_ref``) splits each sequence's
 context into fixed-size token ranges, computes for each range the running
 maximum ``m``, the sum ``l = sum exp(s - m)`` and the unnormalised output
@@ -196,3 +207,40 @@ def decode_partitioned_ref(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarr
         for h in range(hq):
             outs[i, h] = lse_merge_ref(ms[h], ls[h], accs[h])
     return outs
+
+
+def multi_query_ref(q: np.ndarray, q_start: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                    block_tables: np.ndarray, context_lens: np.ndarray, scale: float, q_dtype: str,
+                    kv_dtype: str, k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
+                    seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Causal attention of several new tokens per sequence over its paged cache.
+
+    q: [T, Hq, D], the new tokens of all sequences packed in order; sequence b
+    owns rows [q_start[b], q_start[b+1]), q_len = their count (<= ctx).
+    Token i of sequence b sees positions [0, ctx - q_len + i].  Returns
+    float64 [T, Hq, D] (rows of sequences outside ``seqs`` stay zero).
+    """
+    if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
+        raise ValueError("fp8 caches need k_scale and v_scale")
+    q_start = np.asarray(q_start, dtype=np.int64)
+    n_seq = len(context_lens)
+    if len(q_start) != n_seq + 1 or np.any(np.diff(q_start) < 0) or q_start[0] != 0:
+        raise ValueError("q_start must be a non-decreasing offset list starting at 0")
+    seqs = list(range(n_seq)) if seqs is None else list(seqs)
+    out = np.zeros((q.shape[0], q.shape[1], q.shape[2]), dtype=np.float64)
+    for b in seqs:
+        ctx = int(context_lens[b])
+        q_len = int(q_start[b + 1] - q_start[b])
+        if q_len > ctx:
+            raise ValueError("a sequence has more new tokens than context")
+        k = gather_kv(k_cache, block_tables[b], ctx, kv_dtype, k_scale)
+        v = gather_kv(v_cache, block_tables[b], ctx, kv_dtype, v_scale)
+        for i, pos in enumerate(query_positions(ctx, q_len)):
+            row = int(q_start[b]) + i
+            out[row], _ = attend(to_f64(q[row], q_dtype), k[:, :pos + 1], v[:, :pos + 1], scale)
+    return out
+
+
+def query_positions(ctx: int, q_len: int) -> np.ndarray:
+    """Positions of a sequence's q_len newest tokens: ctx - q_len .. ctx - 1."""
+    return np.arange(ctx - q_len, ctx, dtype=np.int64)

@@ -73,6 +73,9 @@ class PagedWorkload:
     partition_tokens: int = 0
     block_size: int = BLOCK_SIZE
     meta: Dict[str, object] = field(default_factory=dict)
+    # several new tokens per sequence: q is [sum(q_lens), Hq, D] and sequence b
+    # owns rows q_start[b] .. q_start[b+1]-1 (None: one query per sequence)
+    q_start: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -296,6 +299,32 @@ def _extract_new_tokens(rng, q_dtype, kv_dtype, fp8_mode, sigma, table16, k_cach
     if q_dtype == "bf16":
         return _draw_bf16(rng, table16, (T, Hkv, D)), _draw_bf16(rng, table16, (T, Hkv, D))
     return _draw_f32(rng, sigma, (T, Hkv, D)), _draw_f32(rng, sigma, (T, Hkv, D))
+
+
+# ---------------------------------------------------------------------------
+# several new tokens per sequence (chunked prefill, draft verification)
+
+def make_multi_query_workload(*, name: str, seed: int, context_lens: Sequence[int], q_lens: Sequence[int],
+                              num_q_heads: int, num_kv_heads: int, head_dim: int, kv_dtype: str = "bf16",
+                              fp8_mode: str = "values", sigma: float = 0.5,
+                              pool_slack: float = 1.1) -> PagedWorkload:
+    """The layout and pool of ``make_workload`` (one new token per sequence
+    still to be written by a slot scatter), then bf16 queries for the last
+    q_lens[b] positions of every sequence, packed in sequence order.
+
+    Draw order: everything ``make_workload`` draws, then the packed queries.
+    """
+    q_lens = [int(n) for n in q_lens]
+    if len(q_lens) != len(context_lens) or any(n < 0 or n > c for n, c in zip(q_lens, context_lens)):
+        raise ValueError("need 0 <= q_lens[b] <= context_lens[b] for every sequence")
+    rng = np.random.default_rng(seed)
+    wl = make_workload(name=name, seed=seed, context_lens=context_lens, num_q_heads=num_q_heads,
+                       num_kv_heads=num_kv_heads, head_dim=head_dim, q_dtype="bf16", kv_dtype=kv_dtype,
+                       sigma=sigma, pool_slack=pool_slack, fp8_mode=fp8_mode, rng=rng)
+    table16 = _bf16_table(rng, sigma)
+    wl.q = _draw_bf16(rng, table16, (int(sum(q_lens)), num_q_heads, head_dim))
+    wl.q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    return wl
 
 
 # ---------------------------------------------------------------------------

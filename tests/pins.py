@@ -450,10 +450,92 @@ def check_copy_blocks():
         assert np.array_equal(ks2[blk], ks[src]) and np.array_equal(vs2[blk], vs[src])
 
 
+# ---------------------------------------------------------------------------
+# several new query tokens per sequence (chunked prefill, draft verification)
+
+def pack_queries(rng, hq, d, q_lens):
+    q = rng.standard_normal((int(sum(q_lens)), hq, d)).astype(np.float32)
+    q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    return q, q_start
+
+
+def check_multi_query_full_prefill_vs_sdpa_causal(tol=1e-12):
+    """q_len = ctx (a whole prompt): torch float64 SDPA with is_causal=True."""
+    for seed, hq, hkv, d, ctxs in [(141, 4, 4, 16, [1, 16, 17]), (142, 8, 2, 32, [33, 5]),
+                                   (143, 16, 2, 64, [40])]:
+        rng = np.random.default_rng(seed)
+        ks, vs = truth_sequences(rng, hkv, d, ctxs)
+        q, q_start = pack_queries(rng, hq, d, ctxs)
+        kc, vc, bt = page_out(rng, ks, vs)
+        scale = d ** -0.5
+        got = pa.multi_query_ref(q, q_start, kc, vc, bt, np.array(ctxs), scale, "f32", "f32")
+        g = hq // hkv
+        for b, ctx in enumerate(ctxs):
+            qt = torch.from_numpy(q[q_start[b]:q_start[b + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+            kt = torch.from_numpy(ks[b].astype(np.float64)).repeat_interleave(g, dim=0)[None]
+            vt = torch.from_numpy(vs[b].astype(np.float64)).repeat_interleave(g, dim=0)[None]
+            want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+            want = want[0].permute(1, 0, 2).numpy()
+            err = np.abs(got[q_start[b]:q_start[b + 1]] - want).max()
+            assert err < tol, f"seed={seed} seq={b}: |oracle - sdpa causal| = {err}"
+
+
+def check_multi_query_vs_python_bruteforce():
+    """q_len < ctx: pure-Python loops; token i of the chunk sees positions <= ctx - q_len + i."""
+    rng = np.random.default_rng(144)
+    hq, hkv, d, ctxs, q_lens = 4, 2, 4, [20, 9, 33], [3, 1, 5]
+    ks, vs = truth_sequences(rng, hkv, d, ctxs)
+    q, q_start = pack_queries(rng, hq, d, q_lens)
+    kc, vc, bt = page_out(rng, ks, vs)
+    scale = 0.41
+    got = pa.multi_query_ref(q, q_start, kc, vc, bt, np.array(ctxs), scale, "f32", "f32")
+    for b, (ctx, ql) in enumerate(zip(ctxs, q_lens)):
+        for i in range(ql):
+            row = int(q_start[b]) + i
+            visible = ctx - ql + i + 1
+            for h in range(hq):
+                g = h // (hq // hkv)
+                logits = [scale * sum(float(q[row, h, j]) * float(ks[b][g, t, j]) for j in range(d))
+                          for t in range(visible)]
+                top = max(logits)
+                w = [math.exp(s - top) for s in logits]
+                for j in range(d):
+                    want = sum(w[t] * float(vs[b][g, t, j]) for t in range(visible)) / sum(w)
+                    assert abs(got[row, h, j] - want) < 1e-12, (b, i, h, j, got[row, h, j], want)
+
+
+def check_multi_query_chunking_and_decode():
+    """Cutting the new tokens into two chunks (the first chunk seeing a shorter
+    context) changes nothing, and each token equals a one-token decode at its
+    position: chunked prefill and token-by-token decode agree."""
+    rng = np.random.default_rng(145)
+    hq, hkv, d, ctxs, q_lens = 8, 2, 16, [50, 37], [7, 37]
+    ks, vs = truth_sequences(rng, hkv, d, ctxs)
+    q, q_start = pack_queries(rng, hq, d, q_lens)
+    kc, vc, bt = page_out(rng, ks, vs)
+    scale = d ** -0.5
+    whole = pa.multi_query_ref(q, q_start, kc, vc, bt, np.array(ctxs), scale, "f32", "f32")
+    for b, (ctx, ql) in enumerate(zip(ctxs, q_lens)):
+        rows = q[q_start[b]:q_start[b + 1]]
+        cut = ql // 2
+        first = pa.multi_query_ref(rows[:cut], np.array([0, cut]), kc, vc, bt[b:b + 1],
+                                   np.array([ctx - (ql - cut)]), scale, "f32", "f32")
+        second = pa.multi_query_ref(rows[cut:], np.array([0, ql - cut]), kc, vc, bt[b:b + 1],
+                                    np.array([ctx]), scale, "f32", "f32")
+        both = np.concatenate([first, second])
+        assert np.array_equal(both, whole[q_start[b]:q_start[b + 1]]), f"chunking changed sequence {b}"
+        for i in range(ql):
+            pos = ctx - ql + i
+            one = pa.decode_ref(rows[i:i + 1], kc, vc, bt[b:b + 1], np.array([pos + 1]), scale, "f32", "f32")
+            assert np.array_equal(one[0], whole[q_start[b] + i]), f"token {i} of sequence {b} != decode"
+
+
 ALL_CHECKS = [
     check_decode_vs_sdpa, check_decode_vs_python_bruteforce, check_permutation_invariance,
     check_shared_prefix_equivalence, check_special_cases, check_lse, check_partition_merge,
     check_e4m3_table_vs_torch, check_e4m3_known_values, check_e4m3_encode_bruteforce,
     check_e4m3_encode_vs_torch, check_e4m3_quantize_division, check_bf16_vs_torch,
     check_fp8_scaled_decode, check_cache_write_vs_contiguous_append, check_copy_blocks,
+    check_multi_query_full_prefill_vs_sdpa_causal, check_multi_query_vs_python_bruteforce,
+    check_multi_query_chunking_and_decode,
 ]

@@ -121,6 +121,18 @@ def _copy_blocks_swapped(k_cache, v_cache, pairs, k_scale=None, v_scale=None):
     return _real_copy(k_cache, v_cache, p, k_scale, v_scale)
 
 
+def _positions_off_by_one(ctx, q_len):
+    return np.arange(ctx - q_len, ctx, dtype=np.int64) - 1
+
+
+def _positions_top_left(ctx, q_len):
+    return np.arange(0, q_len, dtype=np.int64)
+
+
+def _positions_no_causal_mask(ctx, q_len):
+    return np.full(q_len, ctx - 1, dtype=np.int64)
+
+
 MUTANTS = {
     "gqa_modulo_mapping": (pa, "attend", _attend_mutant(gqa="mod")),
     "scale_dropped": (pa, "attend", _attend_mutant(use_scale=False)),
@@ -137,6 +149,9 @@ MUTANTS = {
     "bf16_wrong_shift": (fm, "bf16_to_f64", _bf16_wrong_shift),
     "cache_write_wrong_offset": (co, "cache_write_ref", _cache_write_wrong_offset),
     "copy_direction_swapped": (co, "copy_blocks_ref", _copy_blocks_swapped),
+    "query_position_off_by_one": (pa, "query_positions", _positions_off_by_one),
+    "causal_mask_top_left": (pa, "query_positions", _positions_top_left),
+    "causal_mask_missing": (pa, "query_positions", _positions_no_causal_mask),
 }
 
 
