@@ -2,9 +2,11 @@
 """Paged-KV decode benchmark on one MI355X.
 
 One step = one decode step of the Llama-3-8B-shaped layer (64 sequences,
-32 query / 8 KV heads, head_dim 128, bf16, contexts U{128..4096}): the slot
-scatter of the 64 new tokens (pa_cache_write) followed by the paged decode
-(pa_decode: partition kernel + log-sum-exp merge).  Inputs are seeded,
+32 query / 8 KV heads, head_dim 128, bf16, contexts U{128..4096}): each
+sequence's new token is written into its slot and the paged decode runs
+over the cache including it.  By default this is one pa_decode_append call
+(the decode kernel writes the new rows itself, then the log-sum-exp merge
+kernel runs); `--step separate` times pa_cache_write + pa_decode instead.  Inputs are seeded,
 synthetic and resident in HBM before timing; the K/V pool is rotated over
 several copies so the 256 MB Infinity Cache cannot hold it between steps.
 
@@ -56,6 +58,10 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--timing-every", type=int, default=8,
+                    help="record HIP events around the decode kernels of one step in this many")
+    ap.add_argument("--step", choices=("append", "separate"), default="append",
+                    help="append: one pa_decode_append call; separate: pa_cache_write then pa_decode")
     return ap.parse_args()
 
 
@@ -211,9 +217,14 @@ def main():
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     steps = []
     for kc, vc in pools:
-        steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
-                      pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale,
-                                        partition_tokens=args.partition_tokens, workspace=ws)))
+        if args.step == "append":
+            steps.append((pa.prepare_decode_append(out, q, new_k, new_v, kc, vc, bt, cl, wl.max_context_len,
+                                                   wl.scale, partition_tokens=args.partition_tokens,
+                                                   workspace=ws),))
+        else:
+            steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
+                          pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale,
+                                            partition_tokens=args.partition_tokens, workspace=ws)))
 
     import oracle
     decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
@@ -226,22 +237,20 @@ def main():
     print(f"# measured stream read {peak_meas:.0f} GB/s", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
-        w, d = steps[i % len(steps)]
-        w()
-        d()
+        for call in steps[i % len(steps)]:
+            call()
     torch.cuda.synchronize()
 
     pa.pa_timing_read()
-    pa.pa_timing_enable(True)
+    pa.pa_timing_enable(args.timing_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        w, d = steps[i % len(steps)]
-        w()
-        d()
+        for call in steps[i % len(steps)]:
+            call()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    pa.pa_timing_enable(False)
+    pa.pa_timing_enable(0)
     part_ms, merge_ms, calls = pa.pa_timing_read()
 
     step_s = (t1 - t0) / args.steps
@@ -277,7 +286,8 @@ def main():
             "pools_rotated": len(pools),
             "work_split": ("balanced slices of the (sequence, block) list" if args.partition_tokens == 0
                            else f"{part}-token partitions"),
-            "step": "pa_cache_write(64 tokens) + pa_decode",
+            "step": ("pa_decode_append: slot write of the 64 new tokens fused into the decode"
+                     if args.step == "append" else "pa_cache_write(64 tokens) + pa_decode"),
         },
         "seqs_per_s": round(wl.num_seqs / step_s, 1),
         "pct_of_spec_hbm": round(100 * value / SPEC_HBM_GBPS, 2),
@@ -286,6 +296,7 @@ def main():
         "step_algorithmic_bytes": int(step_bytes),
         "decode_partition_kernel_ms": round(part_avg_ms, 5),
         "decode_merge_kernel_ms": round(merge_avg_ms, 5),
+        "kernel_timing": f"HIP events on the decode stream around {calls} of the {args.steps} timed steps",
         "roofline": {
             "kernel": "decode partition kernel",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": SPEC_HBM_GBPS, "unit": "GB/s",

@@ -157,6 +157,39 @@ int pa_decode(void* out, const void* q, pa_dtype q_dtype,
               void* stream);
 
 /*
+ * pa_decode_append — one decode step: write each sequence's newest token
+ * into its slot and attend over the cache including it.
+ *
+ * For every sequence b with context_lens[b] = n >= 1, the token at position
+ * n - 1 (slot block_tables[b, (n-1)/16] * 16 + (n-1) % 16) receives
+ * k_new[b, :, :] and v_new[b, :, :] exactly as pa_cache_write would store
+ * them (bit copy, or the e4m3 encode with the block's scale), and out[b] is
+ * what pa_decode returns for the cache after that write.  This is the
+ * decode-time append of "推理优化" section 二 Step 1 (new keys/values
+ * joined to the cache, then attention over all of them) done in one pass:
+ * with a bf16 query and partition_tokens == 0 the wave that reads a
+ * sequence's last block takes the new row from k_new/v_new and writes it to
+ * the cache itself, so no separate scatter kernel runs.  Otherwise the call
+ * runs the scatter and then pa_decode.
+ *
+ * k_new, v_new: [num_seqs, num_kv_heads, head_dim] in q's dtype.  All other
+ * arguments, the workspace rules and the errors are those of pa_decode and
+ * pa_cache_write.  Precondition not checked on the device: the block holding
+ * a sequence's newest token is not shared with another sequence in the
+ * batch (copy-on-write has given it a private copy).
+ */
+int pa_decode_append(void* out, const void* q, pa_dtype q_dtype,
+                     const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, pa_dtype cache_dtype,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t num_blocks, float scale,
+                     int32_t partition_tokens, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * pa_copy_blocks — the copy step of copy-on-write.
  *
  * For every pair i: block block_pairs[i,1] of k_cache and of v_cache becomes
@@ -176,6 +209,93 @@ int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                    void* stream);
 
+/*
+ * Planned attention: several query tokens per sequence, and prefixes shared
+ * between sequences read once.
+ *
+ * pa_decode serves one new token per sequence.  Three other steps attend
+ * over the same paged cache with several new tokens of one sequence at
+ * once: a chunk of a chunked prefill ("17 · 连续批处理与 PagedAttention",
+ * section 二, remedy ① for decode stalls), the K draft tokens a target model
+ * checks in one pass ("推理优化", section 一, speculative decoding), and the
+ * suffix computed after a prefix-cache hit (same section, prefix caching).
+ * The new tokens are the last q_len positions of their sequence, their K/V
+ * are already in the cache (pa_cache_write), and new token i (position
+ * ctx - q_len + i) attends to every position <= its own: the causal mask of
+ * "系统级优化…" section 3.3, aligned to the end of the context.
+ *
+ * Sequences whose block tables start with the same physical blocks share
+ * those blocks' K/V ("17 · 连续批处理与 PagedAttention", section 三: a
+ * shared prefix is stored once and referenced by every sharer; "推理优化"
+ * section 一, prefix caching).  With PA_PLAN_SHARE_PREFIX the plan reads
+ * such a run of blocks once for all sharers (their query columns side by
+ * side in one MFMA tile) and merges that partial result with each sharer's
+ * own suffix by log-sum-exp; the result equals the unshared computation.
+ *
+ * The work is described by a plan built on the host from host copies of
+ * the lengths (and, for prefix sharing, of the block tables), copied by the
+ * caller to device memory, then executed by pa_attend_planned.
+ */
+#define PA_PLAN_SHARE_PREFIX 1
+
+typedef struct pa_plan_info {
+  int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_items;          /* work items (tile of <= 16 query columns, run of blocks), padded */
+  int32_t num_columns;        /* query columns: (new token, query head within its group) */
+  int32_t num_records;        /* partial results, each [num_kv_heads] x (m, l, acc[head_dim]) */
+  int32_t num_merge_rows;     /* columns whose result is merged from partial results */
+  int32_t num_merge_entries;
+  int32_t num_shared_groups;  /* runs of prefix blocks read once for several sequences */
+  int32_t reserved;
+  int64_t plan_bytes;         /* size of the packed plan */
+  int64_t workspace_bytes;    /* scratch pa_attend_planned needs (0: none) */
+  int64_t block_reads;        /* (item, block) pairs: blocks read per KV head */
+} pa_plan_info;
+
+/*
+ * pa_plan_attention — build the plan on the host.
+ *
+ * All arrays are HOST memory.  q_start [num_seqs + 1]: sequence b owns the
+ * new tokens (rows of q) q_start[b] .. q_start[b+1]-1, with q_start[0] == 0
+ * and 0 <= q_len <= context_lens[b]; NULL means one new token per sequence
+ * (q_start[b] = b, the decode case).  context_lens [num_seqs] count every
+ * token of the sequence including the new ones.  block_tables
+ * [num_seqs, max_blocks_per_seq] is read only with PA_PLAN_SHARE_PREFIX
+ * (NULL allowed otherwise).  target_items: how many work items to cut the
+ * work into (0 = automatic).  `plan` receives info->plan_bytes bytes; pass
+ * plan = NULL to learn the sizes only.  Errors: NULL_POINTER, BAD_SHAPE
+ * (inconsistent lengths, context past the block table), UNSUPPORTED
+ * (group > 16, head_dim not 64/128), WORKSPACE (plan_capacity too small).
+ * Pure host computation; thread-safe.
+ */
+int pa_plan_attention(const int32_t* q_start, const int32_t* context_lens,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t flags, int32_t target_items,
+                      void* plan, size_t plan_capacity, pa_plan_info* info);
+
+/*
+ * pa_attend_planned — run a plan.
+ *
+ * out, q: [info->num_q_tokens, num_q_heads, head_dim] bf16 (device).
+ * Caches, scales and block_tables as for pa_decode (device).  `plan` is a
+ * device copy of the bytes pa_plan_attention wrote, and `info` (host) is
+ * the info it returned with them; the shapes in `info` must match the
+ * other arguments.  workspace: at least info->workspace_bytes
+ * bytes of device memory (any contents).  Supported: q BF16 with a BF16 or
+ * FP8_E4M3 cache.  A plan that does not come from pa_plan_attention gives
+ * wrong numbers, not a fault (indices are clamped on the device).  Errors:
+ * NULL_POINTER, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE, MISALIGNED,
+ * LAUNCH.  Writes only `out` and `workspace`.
+ */
+int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype,
+                      const void* k_cache, const void* v_cache, pa_dtype cache_dtype,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, float scale, const void* plan,
+                      const pa_plan_info* info, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* pa_status_string — static text for a status code (never NULL). */
 const char* pa_status_string(int status);
 
@@ -183,13 +303,15 @@ const char* pa_status_string(int status);
  * Measurement hooks (not part of the method; used to report achieved
  * bandwidth against the hardware's).
  *
- * pa_timing_enable(1) makes pa_decode record HIP events on its stream
- * around its partition kernel and its merge kernel; pa_timing_read()
- * waits for the recorded events, returns the summed kernel times in
- * milliseconds and the number of pa_decode calls recorded, and clears
- * the record.  At most 65536 calls are recorded between reads.
+ * pa_timing_enable(n), n >= 1, makes every n-th pa_decode /
+ * pa_decode_append call from then on record HIP events on its stream
+ * around its decode kernel and its merge kernel (n = 0 turns recording
+ * off; sampling keeps the events' own cost out of most calls).
+ * pa_timing_read() waits for the recorded events, returns the summed kernel
+ * times in milliseconds and the number of calls recorded, and clears the
+ * record.  At most 65536 calls are recorded between reads.
  */
-int pa_timing_enable(int enable);
+int pa_timing_enable(int every);
 int pa_timing_read(double* partition_ms, double* merge_ms, int64_t* calls);
 
 /*

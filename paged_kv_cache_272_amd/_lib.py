@@ -11,6 +11,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,19 @@ _lib = _load()
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 
+PA_PLAN_SHARE_PREFIX = 1
+
+
+class PlanInfo(ctypes.Structure):
+    """pa_plan_info (include/pa.h)."""
+    _fields_ = [("num_seqs", _i32), ("num_q_tokens", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
+                ("head_dim", _i32), ("num_items", _i32), ("num_columns", _i32), ("num_records", _i32),
+                ("num_merge_rows", _i32), ("num_merge_entries", _i32), ("num_shared_groups", _i32),
+                ("reserved", _i32), ("plan_bytes", _i64), ("workspace_bytes", _i64), ("block_reads", _i64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
 _SIGNATURES = {
     "pa_cache_write": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                       _i32, _i32, _i32, _i32, _vp]),
@@ -44,11 +58,17 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32,
                                  _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_append": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                        _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(_i64)]),
+    "pa_plan_attention": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                         ctypes.POINTER(PlanInfo)]),
+    "pa_attend_planned": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i32,
+                                         _f32, _vp, ctypes.POINTER(PlanInfo), _vp, _sz, _vp]),
     "pa_probe_sink_bytes": (_sz, []),
     "pa_probe_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "pa_probe_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -131,9 +151,10 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
               partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """out, q [B, Hq, D]; caches [NB, Hkv, 16, D]; block_tables [B, MB] int32; context_lens [B] int32.
 
-    If the call needs scratch and ``workspace`` is None, a zero-filled byte
-    tensor of pa_decode_workspace_size() bytes is allocated on q's device (a
-    caller-provided workspace must be zero-filled before its first use).
+    If the call needs scratch and ``workspace`` is None, a byte tensor of
+    pa_decode_workspace_size() bytes is allocated on q's device.  The
+    workspace needs no initialisation: every byte the merge reads was
+    written by the same call.
     """
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
@@ -144,12 +165,45 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     mb = block_tables.shape[1]
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
                           dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
                           _ptr(context_lens), int(max_context_len), b, hq, hkv, d, num_blocks, float(scale),
                           int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
+
+
+def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        k_scale, v_scale, partition_tokens, workspace, stream):
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    b, hq, d = q.shape
+    num_blocks, hkv, bs, dk = k_cache.shape
+    if bs != BLOCK_SIZE or dk != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch among q, out and the caches")
+    if tuple(k_new.shape) != (b, hkv, d) or k_new.shape != v_new.shape or k_new.dtype != q.dtype:
+        raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim] in q's dtype")
+    need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), int(max_context_len), b, hq, hkv, d, num_blocks, float(scale), int(partition_tokens),
+            _ptr(workspace), ws_bytes, _stream(stream))
+    return args, workspace
+
+
+def pa_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, max_context_len: int, scale: float,
+                     k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                     partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write each sequence's newest token (k_new/v_new [B, Hkv, D], q's dtype) at position
+    context_lens[b] - 1, then decode over the cache including it."""
+    args, _ = _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, scale, k_scale, v_scale, partition_tokens, workspace, stream)
+    _check(_lib.pa_decode_append(*args), "pa_decode_append")
 
 
 def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor,
@@ -164,8 +218,84 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: to
                                _stream(stream)), "pa_copy_blocks")
 
 
-def pa_timing_enable(enable: bool = True) -> None:
-    _check(_lib.pa_timing_enable(1 if enable else 0), "pa_timing_enable")
+def _host_i32(a, name: str) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError(f"{name}: the planner takes host arrays")
+        a = a.numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def pa_plan_attention(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, q_start=None,
+                      block_tables=None, share_prefix: bool = False,
+                      target_items: int = 0) -> Tuple[np.ndarray, PlanInfo]:
+    """Build a plan on the host (host int32 arrays).  Returns (plan bytes, info).
+
+    q_start [B+1] (None: one new token per sequence); block_tables [B, MB]
+    host copy (needed for share_prefix; its width is max_blocks_per_seq).
+    """
+    cl = _host_i32(context_lens, "context_lens")
+    qs = _host_i32(q_start, "q_start")
+    bt = _host_i32(block_tables, "block_tables")
+    b = cl.shape[0]
+    if qs is not None and qs.shape != (b + 1,):
+        raise ValueError("q_start must have num_seqs + 1 entries")
+    mb = bt.shape[1] if bt is not None else max(1, -(-int(cl.max(initial=0)) // BLOCK_SIZE))
+    flags = PA_PLAN_SHARE_PREFIX if share_prefix else 0
+    if share_prefix and bt is None:
+        raise ValueError("share_prefix needs the host block tables")
+    info = PlanInfo()
+    args = [None if qs is None else qs.ctypes.data, cl.ctypes.data, None if bt is None else bt.ctypes.data, mb, b,
+            num_q_heads, num_kv_heads, head_dim, flags, int(target_items)]
+    _check(_lib.pa_plan_attention(*args, None, 0, ctypes.byref(info)), "pa_plan_attention")
+    plan = np.zeros(max(16, info.plan_bytes), dtype=np.uint8)
+    _check(_lib.pa_plan_attention(*args, plan.ctypes.data, plan.nbytes, ctypes.byref(info)), "pa_plan_attention")
+    return plan, info
+
+
+def plan_to_device(plan: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a host plan to device memory (16-byte aligned, as the library requires)."""
+    return torch.from_numpy(plan).to(device)
+
+
+def pa_attend_planned(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, scale: float, plan: torch.Tensor, info: PlanInfo,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out, q [T, Hq, D] bf16; block_tables [B, MB] int32 (device); plan: device copy of the plan bytes."""
+    if block_tables.dtype != torch.int32:
+        raise TypeError("block_tables must be int32")
+    num_blocks, hkv, bs, d = k_cache.shape
+    if bs != BLOCK_SIZE or tuple(q.shape) != (info.num_q_tokens, info.num_q_heads, info.head_dim) \
+            or out.shape != q.shape or hkv != info.num_kv_heads or d != info.head_dim:
+        raise ValueError("tensor shapes do not match the plan")
+    if workspace is None and info.workspace_bytes:
+        workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_attend_planned(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
+                                  dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                  block_tables.shape[1], num_blocks, float(scale), _ptr(plan), ctypes.byref(info),
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "pa_attend_planned")
+
+
+def prepare_attend_planned(out, q, k_cache, v_cache, block_tables, scale, plan, info, k_scale=None, v_scale=None,
+                           workspace=None, stream=None) -> PreparedCall:
+    num_blocks = k_cache.shape[0]
+    if workspace is None and info.workspace_bytes:
+        workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale),
+            _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], num_blocks, float(scale), _ptr(plan),
+            ctypes.byref(info), _ptr(workspace), ws_bytes, _stream(stream))
+    return PreparedCall("pa_attend_planned", args, (out, q, k_cache, v_cache, block_tables, k_scale, v_scale,
+                                                    plan, info, workspace))
+
+
+def pa_timing_enable(every: int = 1) -> None:
+    """Record HIP events around the decode kernels of every `every`-th call (0 = off)."""
+    _check(_lib.pa_timing_enable(int(every)), "pa_timing_enable")
 
 
 def pa_timing_read() -> Tuple[float, float, int]:
@@ -221,7 +351,7 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_con
     num_blocks, hkv, _, _ = k_cache.shape
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
@@ -229,6 +359,16 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_con
             _ptr(workspace), ws_bytes, _stream(stream))
     return PreparedCall("pa_decode", args, (out, q, k_cache, v_cache, block_tables, context_lens, k_scale,
                                             v_scale, workspace))
+
+
+def prepare_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                          scale, k_scale=None, v_scale=None, partition_tokens=0, workspace=None,
+                          stream=None) -> PreparedCall:
+    args, workspace = _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                          max_context_len, scale, k_scale, v_scale, partition_tokens, workspace,
+                                          stream)
+    return PreparedCall("pa_decode_append", args, (out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                                   context_lens, k_scale, v_scale, workspace))
 
 
 def raw_call(name: str, *args):

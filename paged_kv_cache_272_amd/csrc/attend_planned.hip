@@ -1,0 +1,199 @@
+// Executor of a host-built attention plan on the matrix cores (gfx950):
+// several query tokens per sequence with a causal horizon per query column,
+// and prefix blocks shared by several sequences read once for all of them.
+//
+// What is computed: for every query column (new token, query head) the
+// attention of "系统级优化…" section 3.1 over the positions its token sees
+// (the causal mask of section 3.3, aligned to the end of the context), with
+// K/V gathered page by page through the block table (section 2.3).
+//
+// One workgroup per plan item, one wave per KV head.  A wave loads each
+// 16-token K/V block of the item's run once and applies it to the item's
+// (up to 16) query columns as the N dimension of the MFMAs (mfma_tile.h);
+// columns may belong to different tokens of one sequence or to different
+// sequences that share the block.  An item that is its columns' only
+// contribution writes the output; otherwise it leaves (m, l, acc) partials
+// that the merge kernel combines by log-sum-exp.
+//
+// Every index read from the plan is clamped into its array, so a corrupt
+// plan yields wrong numbers rather than an out-of-bounds access.
+#include "mfma_tile.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+template <int D, bool kFp8>
+struct PlannedPending {
+  BlockRegs<D, kFp8> regs;
+  int i;              // logical block
+  float ks, vs;
+};
+
+template <int D, bool kFp8>
+__global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(PlannedArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int g = blockIdx.y * a.waves_per_wg + wave;
+  if (g >= a.num_kv_heads) return;
+  const PlanItem it = a.items[blockIdx.x];
+  const int ncols = min(it.ncols, 16);
+  if (ncols <= 0) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int seq = clampi(it.seq, 0, a.num_seqs - 1);
+
+  // this lane's query column (lanes r >= ncols carry a zero column that sees nothing)
+  PlanColumn col{0, 0, 0, 0};
+  if (r < ncols) col = a.cols[clampi(it.col0 + r, 0, a.num_columns - 1)];
+  const int64_t row = (int64_t)clampi(col.q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
+                      clampi(col.j, 0, G - 1);
+  HeadState<D, kFp8> hs;
+  hs.begin_row(reinterpret_cast<const uint16_t*>(a.q), r < ncols ? row : -1, c);
+
+  const int lo = max(it.blk_lo, 0), hi = min(it.blk_hi, a.max_blocks_per_seq);
+  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+
+  // physical ids and fp8 scales of 64 blocks at a time: lane j holds block idbase + j
+  int idbase = lo - 64, my_blk = 0;
+  float my_ks = 1.0f, my_vs = 1.0f;
+  auto fetch = [&](PlannedPending<D, kFp8>& p, int i) {
+    if (i - idbase >= 64) {
+      idbase += 64;
+      const int bi = idbase + lane;
+      my_blk = bi < hi ? clampi(table[bi], 0, a.num_blocks - 1) : 0;
+      if constexpr (kFp8) {
+        my_ks = bi < hi ? a.k_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
+        my_vs = bi < hi ? a.v_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
+      }
+    }
+    const int j = i - idbase;
+    p.i = i;
+    if constexpr (kFp8) {
+      p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), j));
+      p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), j));
+    } else {
+      p.ks = p.vs = 1.0f;
+    }
+    load_block<D, kFp8>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(my_blk, j), a.num_kv_heads, g, r, c);
+  };
+  auto consume = [&](const PlannedPending<D, kFp8>& p) {
+    const int t0 = p.i * kBlockTokens;
+    const int valid = min(kBlockTokens, it.kv_len - t0);
+    hs.step_cols(p.regs, valid, col.horizon - t0, a.scale_log2 * p.ks, p.vs, c);
+  };
+
+  // software pipeline: the next block's loads are in flight while this one computes
+  PlannedPending<D, kFp8> p0, p1;
+  if (lo < hi) fetch(p0, lo);
+  for (int i = lo; i < hi; i += 2) {
+    if (i + 1 < hi) fetch(p1, i + 1);
+    consume(p0);
+    if (i + 1 < hi) {
+      if (i + 2 < hi) fetch(p0, i + 2);
+      consume(p1);
+    }
+  }
+
+  const float L = hs.total_l();
+  float o[4 * Tile<D, kFp8>::kE];
+  hs.unpack(o);
+  if (r >= ncols) return;
+  const int d0 = (D / 4) * c;
+  if (it.rec0 < 0) {
+    store_bf16_run<D>(reinterpret_cast<uint16_t*>(a.out) + row * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
+  } else {
+    const int64_t wr = (int64_t)clampi(it.rec0 + r, 0, a.num_records - 1) * a.num_kv_heads + g;
+    store_f32_run<D>(a.ws_acc + wr * D, d0, o);
+    if (c == 0) {
+      a.ws_m[wr] = hs.m;
+      a.ws_l[wr] = L;
+    }
+  }
+}
+
+// out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's
+// records (M = max_k m_k; records whose column saw no token have m = -inf
+// and weigh nothing).  One thread per (KV head, 4-wide chunk) of the row.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(PlannedArgs a) {
+  constexpr int kChunks = D / 4;
+  const int t = blockIdx.y * kMergeThreads + threadIdx.x;
+  const int g = t / kChunks, ch = t % kChunks;
+  if (g >= a.num_kv_heads) return;
+  const PlanMergeRow mr = a.rows[blockIdx.x];
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int e0 = clampi(mr.e0, 0, a.num_merge_entries), e1 = clampi(mr.e0 + mr.n, e0, a.num_merge_entries);
+  float M = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int e = e0; e < e1; e += 4) {
+    float mv[4], lv[4];
+    float4 av[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      mv[k] = -INFINITY;
+      lv[k] = 0.0f;
+      av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (e + k < e1) {
+        const int64_t wr = (int64_t)clampi(a.entries[e + k], 0, a.num_records - 1) * a.num_kv_heads + g;
+        mv[k] = a.ws_m[wr];
+        if (mv[k] != -INFINITY) {
+          lv[k] = a.ws_l[wr];
+          av[k] = reinterpret_cast<const float4*>(a.ws_acc + wr * D)[ch];
+        }
+      }
+    }
+    const float Mn = fmaxf(M, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    if (Mn == -INFINITY) continue;                              // nothing seen yet
+    const float sc = __builtin_amdgcn_exp2f(M - Mn);            // 0 while M is -inf
+    den *= sc;
+    num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float wt = __builtin_amdgcn_exp2f(mv[k] - Mn);      // 0 for empty records
+      den += wt * lv[k];
+      num.x += wt * av[k].x; num.y += wt * av[k].y; num.z += wt * av[k].z; num.w += wt * av[k].w;
+    }
+    M = Mn;
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  const int64_t orow = (int64_t)clampi(mr.q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
+                       clampi(mr.j, 0, G - 1);
+  const uint2 packed = make_uint2(f32_to_bf16_bits_rne(num.x * inv) | (f32_to_bf16_bits_rne(num.y * inv) << 16),
+                                  f32_to_bf16_bits_rne(num.z * inv) | (f32_to_bf16_bits_rne(num.w * inv) << 16));
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow * D + 4 * ch) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_items, a.head_groups);
+  const dim3 block(64 * a.waves_per_wg);
+  const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
+  if (a.head_dim == 128) {
+    if (fp8) hipLaunchKernelGGL((attend_planned_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attend_planned_kernel<128, false>), grid, block, 0, stream, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((attend_planned_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attend_planned_kernel<64, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_planned_merge(const PlannedArgs& a, hipStream_t stream) {
+  const int per_row = a.num_kv_heads * (a.head_dim / 4);
+  const dim3 grid(a.num_merge_rows, (per_row + kMergeThreads - 1) / kMergeThreads);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((attend_planned_merge_kernel<128>), grid, dim3(kMergeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attend_planned_merge_kernel<64>), grid, dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -17,11 +17,20 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kWriteThreads = 128;
 
+// Slot of token t: given, or the newest position of sequence t.
+__device__ __forceinline__ int64_t token_slot(const CacheWriteArgs& a, int t) {
+  if (a.slot_mapping) return a.slot_mapping[t];
+  const int ctx = a.context_lens[t];
+  if (ctx <= 0 || ctx > a.max_blocks_per_seq * kBlockTokens) return -1;
+  const int blk = a.block_tables[(int64_t)t * a.max_blocks_per_seq + (ctx - 1) / kBlockTokens];
+  return (int64_t)blk * kBlockTokens + (ctx - 1) % kBlockTokens;
+}
+
 // Copy one token's [Hkv, D] row (bit copy; f32 or bf16).
 __global__ __launch_bounds__(kWriteThreads) void cache_write_copy_kernel(CacheWriteArgs a, int elem_bytes) {
   const int t = blockIdx.x;
   const bool is_v = blockIdx.y != 0;
-  const int64_t slot = a.slot_mapping[t];
+  const int64_t slot = token_slot(a, t);
   if (slot < 0 || slot >= (int64_t)a.num_blocks * kBlockTokens) return;
   const int64_t blk = slot / kBlockTokens;
   const int off = (int)(slot % kBlockTokens);
@@ -41,7 +50,7 @@ template <bool kSrcBf16>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_fp8_kernel(CacheWriteArgs a) {
   const int t = blockIdx.x;
   const bool is_v = blockIdx.y != 0;
-  const int64_t slot = a.slot_mapping[t];
+  const int64_t slot = token_slot(a, t);
   if (slot < 0 || slot >= (int64_t)a.num_blocks * kBlockTokens) return;
   const int64_t blk = slot / kBlockTokens;
   const int off = (int)(slot % kBlockTokens);

@@ -10,259 +10,25 @@
 // all G query heads of that head's group at once: the query heads are the N
 // dimension of the MFMAs, so a block is read from HBM once per group.
 //
-// Per block (16 tokens), lane l = 16*c + r (r = l%16, c = l/16):
-//   QK:  S^T[token][head] = K[token][:] . Q[head][:]  with D/32 MFMAs
-//        16x16x32 bf16.  A = K: lane holds 8 consecutive d of token r
-//        (row r), B = Q^T: lane holds the same 8 d of head r.  The d chunk
-//        for k-step i and lane group c is (D/32)*c + i, so a lane reads one
-//        contiguous D/4-element run of its token's row.
-//        Result: lane holds s[j] = S^T[token 4c+j][head r], j = 0..3.
-//   softmax: scale, mask past the context by select, block max over the
-//        4 lane groups (permlane swaps), running max / sum update; the
-//        output is rescaled only when some running max grew.
-//   PV:  O^T[d][head] += V^T[d][token] . P^T[token][head] with D/16 MFMAs
-//        16x16x16 bf16.  B = P^T: lane holds p[j] for tokens 4c..4c+3 of
-//        head r, which is exactly the QK result layout, so P never leaves
-//        registers.  A = V^T: lane holds tokens 4c..4c+3 of one d; V is
-//        loaded row-contiguously (16 lanes per 256-byte token row) and the
-//        4x(D/16) sub-tile is transposed in registers with byte permutes.
-//        Tile n covers d = (D/16)*r + n, so lane (r, c) ends up holding the
-//        contiguous output run d in [(D/4)c, (D/4)(c+1)) of head r.
-// e4m3 codes are widened to bf16 exactly (every e4m3 value is a bf16
-// value); the per-(block, head) scales multiply the logits (K) and the
-// probabilities fed to P.V (V).
+// The register layout of a block, the two MFMA contractions and the online
+// softmax are in mfma_tile.h.
 //
 // Two work splits (see DecodeArgs): a partition grid, and a balanced split
 // in which every workgroup takes an equal slice of all (sequence, block)
 // units, so no compute unit idles at the end of the launch.
+#include "mfma_tile.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kPartWaves = 4;
 constexpr int kPartThreads = 64 * kPartWaves;
-
-// All-reduce over the lane pairs (l, l^32) and (l, l^16): each permlane swap
-// returns, per lane, its own value and its partner's (in some order).
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Two e4m3 codes (bytes 0,1 or 2,3 of `w`) -> two bf16 values, exactly.
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
-  const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
-  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-}
 
 __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int b) {
   const int ctx = a.context_lens[b];
   return ctx < 0 ? 0 : min(min(ctx, a.max_context_len), a.max_blocks_per_seq * kBlockTokens);
-}
-
-template <int D, bool kFp8>
-struct Tile {
-  static constexpr int kKSteps = D / 32;                  // QK MFMAs (16x16x32)
-  static constexpr int kE = D / 16;                       // V elements per lane per token = PV MFMAs
-  static constexpr int kEb = kFp8 ? 1 : 2;
-  static constexpr int kKWords = kKSteps * 8 * kEb / 4;   // K words per lane per block
-  static constexpr int kVWords = kE * kEb / 4;            // V words per lane per token
-};
-
-// Load `W` 32-bit words from a 4*W-byte aligned address.
-template <int W>
-__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
-  if constexpr (W % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (W == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  } else {
-    static_assert(W == 1, "unsupported load width");
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
-
-// One 16-token K/V block of one KV head, as this lane holds it.
-template <int D, bool kFp8>
-struct BlockRegs {
-  uint32_t k[Tile<D, kFp8>::kKWords];
-  uint32_t v[4][Tile<D, kFp8>::kVWords];
-};
-
-template <int D, bool kFp8>
-__device__ __forceinline__ void load_block(BlockRegs<D, kFp8>& br, const uint8_t* kbase, const uint8_t* vbase,
-                                           int64_t blk, int num_kv_heads, int g, int r, int c) {
-  using T = Tile<D, kFp8>;
-  const int64_t head_base = (blk * num_kv_heads + g) * kBlockTokens;            // token row index
-  load_words<T::kKWords>(kbase + ((head_base + r) * D + (D / 4) * c) * T::kEb, br.k);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    load_words<T::kVWords>(vbase + ((head_base + 4 * c + e) * D + T::kE * r) * T::kEb, br.v[e]);
-}
-
-// Running state of one wave: G query heads of one KV head over a run of blocks.
-template <int D, bool kFp8>
-struct HeadState {
-  using T = Tile<D, kFp8>;
-  static constexpr int kE = T::kE;
-  bf16x8_t qop[T::kKSteps];
-  f32x4_t acc[kE];
-  float m, l;
-
-  // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
-  __device__ __forceinline__ void begin(const uint16_t* q, int64_t q_row0, int G, int r, int c) {
-    const uint16_t* qp = q + (q_row0 + r) * D + (D / 4) * c;
-#pragma unroll
-    for (int i = 0; i < T::kKSteps; ++i) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (r < G) w = reinterpret_cast<const uint4*>(qp)[i];
-      qop[i] = __builtin_bit_cast(bf16x8_t, w);
-    }
-    m = -INFINITY;
-    l = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kE; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  // Fold one block in.  `valid` = tokens of the block inside the context
-  // (1..16), `sc` = scale*log2(e) (times the block's K scale for e4m3),
-  // `vs` = the block's V scale.
-  __device__ __forceinline__ void step(const BlockRegs<D, kFp8>& br, int valid, float sc, float vs, int c) {
-    // ---- S^T = K . Q^T
-    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int st = 0; st < T::kKSteps; ++st) {
-      uint4 kw;
-      if constexpr (kFp8) {
-        kw = make_uint4(fp8x2_to_bf16x2(br.k[2 * st], false), fp8x2_to_bf16x2(br.k[2 * st], true),
-                        fp8x2_to_bf16x2(br.k[2 * st + 1], false), fp8x2_to_bf16x2(br.k[2 * st + 1], true));
-      } else {
-        kw = make_uint4(br.k[4 * st], br.k[4 * st + 1], br.k[4 * st + 2], br.k[4 * st + 3]);
-      }
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
-    }
-    float sv[4] = {s[0] * sc, s[1] * sc, s[2] * sc, s[3] * sc};
-    uint32_t vmask = 0xfu;                                        // tokens 4c+e kept for P.V (bit e)
-    if (valid < kBlockTokens) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * c + j >= valid) sv[j] = -INFINITY;
-      vmask = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vmask |= (4 * c + e < valid) ? (1u << e) : 0u;
-    }
-    // ---- online softmax (base 2)
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = max_xor16(max_xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    if (__ballot(m_new > m) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int t = 0; t < kE; ++t) acc[t] *= alpha;
-      m = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    const short4_t pop = __builtin_bit_cast(
-        short4_t, make_uint2(pack_bf16x2(p[0] * vs, p[1] * vs), pack_bf16x2(p[2] * vs, p[3] * vs)));
-    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n).  Masked
-    // tokens get V = 0 by selection (their slots may hold NaN).
-    uint32_t vw[4][T::kVWords];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int w = 0; w < T::kVWords; ++w) vw[e][w] = (vmask >> e & 1u) ? br.v[e][w] : 0u;
-#pragma unroll
-    for (int nn = 0; nn < kE; ++nn) {
-      uint32_t lo, hi;
-      if constexpr (kFp8) {
-        // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
-        const int w = nn / 4, byte = nn % 4;
-        const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
-        const uint32_t c01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
-        const uint32_t c23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
-        lo = fp8x2_to_bf16x2(c01, false);
-        hi = fp8x2_to_bf16x2(c23, false);
-      } else {
-        const int w = nn / 2;
-        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-        lo = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
-        hi = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
-      }
-      const short4_t vop = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
-      acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[nn], 0, 0, 0);
-    }
-  }
-
-  // The wave's total sum (the 4 lane groups hold partial sums of one head).
-  __device__ __forceinline__ float total_l() const { return sum_xor16(sum_xor32(l)); }
-
-  // Output run of this lane: d = (D/4)*c + kE*j + n  ->  o[kE*j + n].
-  __device__ __forceinline__ void unpack(float* o) const {
-#pragma unroll
-    for (int nn = 0; nn < kE; ++nn)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[kE * j + nn] = acc[nn][j];
-  }
-};
-
-// Write D/4 normalised values of one query row as bf16 (16-byte stores).
-template <int D>
-__device__ __forceinline__ void store_bf16_run(uint16_t* dst_row, int d0, const float* o, float inv) {
-  uint32_t* dst = reinterpret_cast<uint32_t*>(dst_row + d0);
-#pragma unroll
-  for (int i = 0; i < D / 8; i += 4) {
-    const uint4 w = make_uint4(pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv),
-                               pack_bf16x2(o[2 * i + 2] * inv, o[2 * i + 3] * inv),
-                               pack_bf16x2(o[2 * i + 4] * inv, o[2 * i + 5] * inv),
-                               pack_bf16x2(o[2 * i + 6] * inv, o[2 * i + 7] * inv));
-    *reinterpret_cast<uint4*>(dst + i) = w;
-  }
-}
-
-// Write D/4 unnormalised fp32 values of one workspace row.
-template <int D>
-__device__ __forceinline__ void store_f32_run(float* dst_row, int d0, const float* o) {
-  float4* dst = reinterpret_cast<float4*>(dst_row + d0);
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,8 +154,17 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------
 // Balanced split.  Units are (sequence, 16-token block) pairs laid end to end
 // in sequence order; sequence b owns units [start[b], start[b+1]).  Workgroup
-// x takes units [x*per, (x+1)*per), per = ceil(U / num_wgs); wave w of
+// x takes units [floor(x*U/n), floor((x+1)*U/n)) (n = min(num_wgs, U)); wave w of
 // workgroup (x, y) handles KV head y*waves + w over that slice.
+
+// n = min(workgroups, U) slices, so none is empty; slice x covers units
+// [floor(x*U/n), floor((x+1)*U/n)): sizes differ by at most one.
+__device__ __forceinline__ int num_slices(int U, int num_wgs) { return min(U, num_wgs); }
+__device__ __forceinline__ int slice_begin(int x, int U, int n) { return (int)((int64_t)x * U / n); }
+// The slice holding unit u: the largest x with slice_begin(x) <= u.
+__device__ __forceinline__ int slice_of(int u, int U, int n) {
+  return (int)(((int64_t)(u + 1) * n + U - 1) / U) - 1;
+}
 
 struct UnitIds {
   int b, i, blk;       // lane j: the (sequence, logical block, physical block) of unit base + j
@@ -427,8 +202,12 @@ __device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* star
 template <int D, bool kFp8>
 struct Pending {
   BlockRegs<D, kFp8> regs;
+  int64_t blk;
   int b, i;
   float ks, vs;
+  int off;                  // appending: slot of the sequence's newest token in this block, else -1
+  uint32_t nk[D / 8];       // its K run (lane r == off) as bf16 pairs
+  uint32_t nv[D / 32];      // its V run (lane group c == off / 4) as bf16 pairs
 };
 
 template <int D, bool kFp8>
@@ -477,8 +256,8 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
   if (tid == 0) s_start[B] = carry;
   __syncthreads();
   const int U = carry;
-  const int per = (U + a.num_wgs - 1) / a.num_wgs;
-  const int u0 = min(U, x * per), u1 = min(U, u0 + per);
+  const int ns = num_slices(U, a.num_wgs);               // workgroups x >= ns have no slice
+  const int u0 = x < ns ? slice_begin(x, U, ns) : U, u1 = x < ns ? slice_begin(x + 1, U, ns) : U;
   if (x == 0 && y == 0)
     for (int b = tid; b <= B; b += W * 64) a.ws_seq_start[b] = s_start[b];
 
@@ -533,20 +312,69 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
     const int j = u - base;
     p.b = __builtin_amdgcn_readlane(cur.b, j);
     p.i = __builtin_amdgcn_readlane(cur.i, j);
+    p.blk = __builtin_amdgcn_readlane(cur.blk, j);
     if constexpr (kFp8) {
       p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
       p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
     } else {
       p.ks = p.vs = 1.0f;
     }
-    load_block<D, kFp8>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(cur.blk, j), a.num_kv_heads, g, r, c);
+    p.off = -1;
+    if (a.append) {
+      const int ctx = s_ctx[p.b];
+      if ((p.i + 1) * kBlockTokens >= ctx) {          // the sequence's last block holds its newest token
+        p.off = (ctx - 1) % kBlockTokens;
+        // every lane loads its runs of the new row; only lane r == off (K) and
+        // lane group off/4 (V) use them
+        const int64_t row = ((int64_t)p.b * a.num_kv_heads + g) * D;
+        load_words<D / 8>(reinterpret_cast<const uint8_t*>(reinterpret_cast<const uint16_t*>(a.k_new) + row + d0),
+                          p.nk);
+        load_words<D / 32>(reinterpret_cast<const uint8_t*>(reinterpret_cast<const uint16_t*>(a.v_new) + row +
+                                                            (D / 16) * r),
+                           p.nv);
+      }
+    }
+    load_block<D, kFp8>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
   };
-  auto consume = [&](const Pending<D, kFp8>& p) {
+  // Appending: put the newest token's K/V row into the block this wave holds
+  // and into its slot in the cache (the wave that reads a block is the only
+  // reader of that slot in this launch).
+  auto splice = [&](Pending<D, kFp8>& p) {
+    using T = Tile<D, kFp8>;
+    const int64_t head_base = (p.blk * a.num_kv_heads + g) * kBlockTokens;
+    uint8_t* kw = const_cast<uint8_t*>(kbase);
+    uint8_t* vw = const_cast<uint8_t*>(vbase);
+    if (r == p.off) {
+      uint32_t words[T::kKWords];
+      if constexpr (kFp8) quantize_bf16_words<D / 4>(p.nk, p.ks, words);
+      else
+#pragma unroll
+        for (int w = 0; w < T::kKWords; ++w) words[w] = p.nk[w];
+#pragma unroll
+      for (int w = 0; w < T::kKWords; ++w) p.regs.k[w] = words[w];
+      store_words<T::kKWords>(kw + ((head_base + r) * D + d0) * T::kEb, words);
+    }
+    uint32_t words[T::kVWords];
+    if constexpr (kFp8) quantize_bf16_words<D / 16>(p.nv, p.vs, words);
+    else
+#pragma unroll
+      for (int w = 0; w < T::kVWords; ++w) words[w] = p.nv[w];
+    // token 4c + ee of this lane's V rows is the new one (by selection: no register indexing)
+#pragma unroll
+    for (int ee = 0; ee < 4; ++ee) {
+      const bool hit = 4 * c + ee == p.off;
+#pragma unroll
+      for (int w = 0; w < T::kVWords; ++w) p.regs.v[ee][w] = hit ? words[w] : p.regs.v[ee][w];
+    }
+    if (c == p.off / 4) store_words<T::kVWords>(vw + ((head_base + p.off) * D + T::kE * r) * T::kEb, words);
+  };
+  auto consume = [&](Pending<D, kFp8>& p) {
     if (p.b != cur_b) {
       if (cur_b >= 0) finish(cur_b);
       cur_b = p.b;
       hs.begin(q, (int64_t)p.b * a.num_q_heads + (int64_t)g * G, G, r, c);
     }
+    if (p.off >= 0) splice(p);
     const int valid = min(kBlockTokens, s_ctx[p.b] - p.i * kBlockTokens);
     hs.step(p.regs, valid, a.scale_log2 * p.ks, p.vs, c);
   };
@@ -582,8 +410,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_balanced_kernel(De
   const int U = a.ws_seq_start[a.num_seqs];
   const int s = a.ws_seq_start[b], e = a.ws_seq_start[b + 1];
   if (s == e) return;                                  // empty: zero row written by the decode kernel
-  const int per = (U + a.num_wgs - 1) / a.num_wgs;
-  const int wf = s / per, wl = (e - 1) / per;
+  const int ns = num_slices(U, a.num_wgs);
+  const int wf = slice_of(s, U, ns), wl = slice_of(e - 1, U, ns);
   if (wf == wl) return;                                // written whole by its slice
   const int n = wl - wf + 1;
   const int h = it / kChunks, ch = it % kChunks;

@@ -202,11 +202,22 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-// Merge: one workgroup of D threads per (query head, sequence).
+// Merge: one workgroup per (query head, sequence).  Thread (lp, ch) owns the
+// 4-wide output chunk ch and the partitions lp, lp + P', ... (P' = 256 / (D/4)
+// partition lanes), folded with a running maximum four at a time so their
+// loads are in flight together; the partition lanes are combined in LDS.
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+constexpr int kMergeThreads = 256;
+
 template <bool kQBf16, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kChunks = D / 4;
+  constexpr int kLanesP = kMergeThreads / kChunks;
+  __shared__ float s_m[kLanesP][kChunks];
+  __shared__ float s_l[kLanesP][kChunks];
+  __shared__ float4 s_acc[kLanesP][kChunks];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int ch = threadIdx.x % kChunks, lp = threadIdx.x / kChunks;
   const int P = a.partition_tokens;
   const int ctx = seq_context(a, b);
   const int nparts = (ctx + P - 1) / P;
@@ -214,16 +225,60 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = (int64_t)b * a.num_q_heads + h;
   const float* m = a.ws_m + row * a.num_parts;
   const float* l = a.ws_l + row * a.num_parts;
-  const float* acc = a.ws_acc + row * a.num_parts * D;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, m[p]);
-  float num = 0.0f, den = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = exp2f(m[p] - M);
-    den += w * l[p];
-    num += w * acc[(int64_t)p * D + d];
+  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + row * a.num_parts * D);
+  float M = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int p0 = lp; p0 < nparts; p0 += 4 * kLanesP) {
+    float mv[4], lv[4];
+    float4 av[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + k * kLanesP;
+      if (p < nparts) {
+        mv[k] = m[p];
+        lv[k] = l[p];
+        av[k] = acc[(int64_t)p * kChunks + ch];
+      } else {
+        mv[k] = -INFINITY;
+        lv[k] = 0.0f;
+        av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+    const float Mn = fmaxf(M, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    const float sc = exp2f(M - Mn);                 // 0 while M is still -inf
+    den *= sc;
+    num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float w = exp2f(mv[k] - Mn);            // 0 for the padding entries
+      den += w * lv[k];
+      num.x += w * av[k].x; num.y += w * av[k].y; num.z += w * av[k].z; num.w += w * av[k].w;
+    }
+    M = Mn;
   }
-  store_out<kQBf16>(a.out, row * D + d, num / den);
+  s_m[lp][ch] = M;
+  s_l[lp][ch] = den;
+  s_acc[lp][ch] = num;
+  __syncthreads();
+  if (lp != 0) return;
+  float MM = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kLanesP; ++i) MM = fmaxf(MM, s_m[i][ch]);
+  float dd = 0.0f;
+  float4 nn = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int i = 0; i < kLanesP; ++i) {
+    const float w = s_m[i][ch] == -INFINITY ? 0.0f : exp2f(s_m[i][ch] - MM);   // lanes without partitions
+    dd += w * s_l[i][ch];
+    const float4 v = s_acc[i][ch];
+    nn.x += w * v.x; nn.y += w * v.y; nn.z += w * v.z; nn.w += w * v.w;
+  }
+  const float inv = 1.0f / dd;
+  const int64_t o = row * D + 4 * ch;
+  store_out<kQBf16>(a.out, o, nn.x * inv);
+  store_out<kQBf16>(a.out, o + 1, nn.y * inv);
+  store_out<kQBf16>(a.out, o + 2, nn.z * inv);
+  store_out<kQBf16>(a.out, o + 3, nn.w * inv);
 }
 
 template <bool kQBf16, int KV>
@@ -252,12 +307,13 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.num_seqs);
   const bool bf16 = a.q_dtype == PA_DTYPE_BF16;
+  const dim3 block(kMergeThreads);
   if (a.head_dim == 64) {
-    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a);
+    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 64>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, block, 0, stream, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(128), 0, stream, a);
-    else hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(128), 0, stream, a);
+    if (bf16) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,330 @@
+// Register-level building blocks of the MFMA paged-attention kernels
+// (gfx950): one 16-token K/V block of one KV head held by a wave, the query
+// operand of up to 16 query columns, and the online-softmax state.
+//
+// Layout, per block, with lane l = 16*c + r (r = l%16, c = l/16):
+//   QK:  S^T[token][column] = K[token][:] . Q[column][:]  with D/32 MFMAs
+//        16x16x32 bf16.  A = K: lane holds 8 consecutive d of token r
+//        (row r), B = Q^T: lane holds the same 8 d of query column r.  The d
+//        chunk for k-step i and lane group c is (D/32)*c + i, so a lane reads
+//        one contiguous D/4-element run of its token's row.
+//        Result: lane holds s[j] = S^T[token 4c+j][column r], j = 0..3.
+//   softmax: scale, mask by select, block max over the 4 lane groups
+//        (permlane swaps), running max / sum update; the output is rescaled
+//        only when some running max grew.
+//   PV:  O^T[d][column] += V^T[d][token] . P^T[token][column] with D/16
+//        MFMAs 16x16x16 bf16.  B = P^T: lane holds p[j] for tokens 4c..4c+3
+//        of column r, which is exactly the QK result layout, so P never
+//        leaves registers.  A = V^T: lane holds tokens 4c..4c+3 of one d; V
+//        is loaded row-contiguously (16 lanes per 256-byte token row) and the
+//        4x(D/16) sub-tile is transposed in registers with byte permutes.
+//        Tile n covers d = (D/16)*r + n, so lane (r, c) ends up holding the
+//        contiguous output run d in [(D/4)c, (D/4)(c+1)) of column r.
+// e4m3 codes are widened to bf16 exactly (every e4m3 value is a bf16
+// value); the per-(block, head) scales multiply the logits (K) and the
+// probabilities fed to P.V (V).
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+
+// All-reduce over the lane pairs (l, l^32) and (l, l^16): each permlane swap
+// returns, per lane, its own value and its partner's (in some order).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two e4m3 codes (bytes 0,1 or 2,3 of `w`) -> two bf16 values, exactly.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
+  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+
+template <int D, bool kFp8>
+struct Tile {
+  static constexpr int kKSteps = D / 32;                  // QK MFMAs (16x16x32)
+  static constexpr int kE = D / 16;                       // V elements per lane per token = PV MFMAs
+  static constexpr int kEb = kFp8 ? 1 : 2;
+  static constexpr int kKWords = kKSteps * 8 * kEb / 4;   // K words per lane per block
+  static constexpr int kVWords = kE * kEb / 4;            // V words per lane per token
+};
+
+// Load `W` 32-bit words from a 4*W-byte aligned address.
+template <int W>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (W == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    static_assert(W == 1, "unsupported load width");
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Store `W` 32-bit words to a 4*W-byte aligned address.
+template <int W>
+__device__ __forceinline__ void store_words(uint8_t* p, const uint32_t* w) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i)
+      reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (W == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+    static_assert(W == 1, "unsupported store width");
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+  }
+}
+
+// NV bf16 values (NV/2 words) -> NV e4m3 codes (NV/4 words) of x / scale,
+// IEEE division, saturating round-to-nearest-even (as the slot scatter does).
+template <int NV>
+__device__ __forceinline__ void quantize_bf16_words(const uint32_t* src, float scale, uint32_t* dst) {
+#pragma unroll
+  for (int i = 0; i < NV / 4; ++i) {
+    uint32_t code = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int v = 4 * i + k;
+      const uint32_t bits = (v & 1) ? (src[v / 2] >> 16) : (src[v / 2] & 0xffffu);
+      code |= f32_to_e4m3_sat_rne(__fdiv_rn(bf16_bits_to_f32(bits), scale)) << (8 * k);
+    }
+    dst[i] = code;
+  }
+}
+
+// One 16-token K/V block of one KV head, as this lane holds it.
+template <int D, bool kFp8>
+struct BlockRegs {
+  uint32_t k[Tile<D, kFp8>::kKWords];
+  uint32_t v[4][Tile<D, kFp8>::kVWords];
+};
+
+template <int D, bool kFp8>
+__device__ __forceinline__ void load_block(BlockRegs<D, kFp8>& br, const uint8_t* kbase, const uint8_t* vbase,
+                                           int64_t blk, int num_kv_heads, int g, int r, int c) {
+  using T = Tile<D, kFp8>;
+  const int64_t head_base = (blk * num_kv_heads + g) * kBlockTokens;            // token row index
+  load_words<T::kKWords>(kbase + ((head_base + r) * D + (D / 4) * c) * T::kEb, br.k);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    load_words<T::kVWords>(vbase + ((head_base + 4 * c + e) * D + T::kE * r) * T::kEb, br.v[e]);
+}
+
+// Running state of one wave: G query heads of one KV head over a run of blocks.
+template <int D, bool kFp8>
+struct HeadState {
+  using T = Tile<D, kFp8>;
+  static constexpr int kE = T::kE;
+  bf16x8_t qop[T::kKSteps];
+  f32x4_t acc[kE];
+  float m, l;
+
+  // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
+  __device__ __forceinline__ void begin(const uint16_t* q, int64_t q_row0, int G, int r, int c) {
+    const uint16_t* qp = q + (q_row0 + r) * D + (D / 4) * c;
+#pragma unroll
+    for (int i = 0; i < T::kKSteps; ++i) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (r < G) w = reinterpret_cast<const uint4*>(qp)[i];
+      qop[i] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    reset();
+  }
+
+  // Q^T operand with an arbitrary query row per column: lane r takes row
+  // `row` (-1: a zero column).
+  __device__ __forceinline__ void begin_row(const uint16_t* q, int64_t row, int c) {
+    const uint16_t* qp = q + (row < 0 ? 0 : row) * D + (D / 4) * c;
+#pragma unroll
+    for (int i = 0; i < T::kKSteps; ++i) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row >= 0) w = reinterpret_cast<const uint4*>(qp)[i];
+      qop[i] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    reset();
+  }
+
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kE; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // Fold one block in.  `valid` = tokens of the block inside the context
+  // (1..16), `sc` = scale*log2(e) (times the block's K scale for e4m3),
+  // `vs` = the block's V scale.  Every column sees the same tokens.
+  __device__ __forceinline__ void step(const BlockRegs<D, kFp8>& br, int valid, float sc, float vs, int c) {
+    step_impl<false>(br, valid, 0, sc, vs, c);
+  }
+
+  // Fold one block in with a causal horizon per column: column r (this
+  // lane's) sees only the block's first `col_valid` tokens (any integer;
+  // <= 0 hides the whole block, >= 16 hides nothing).  `valid` still bounds
+  // the tokens whose V rows hold data.  A column may see no token at all
+  // (then m stays -inf, l = 0, acc = 0).
+  __device__ __forceinline__ void step_cols(const BlockRegs<D, kFp8>& br, int valid, int col_valid, float sc,
+                                            float vs, int c) {
+    step_impl<true>(br, valid, col_valid, sc, vs, c);
+  }
+
+  template <bool kCols>
+  __device__ __forceinline__ void step_impl(const BlockRegs<D, kFp8>& br, int valid, int col_valid, float sc,
+                                            float vs, int c) {
+    // ---- S^T = K . Q^T
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < T::kKSteps; ++st) {
+      uint4 kw;
+      if constexpr (kFp8) {
+        kw = make_uint4(fp8x2_to_bf16x2(br.k[2 * st], false), fp8x2_to_bf16x2(br.k[2 * st], true),
+                        fp8x2_to_bf16x2(br.k[2 * st + 1], false), fp8x2_to_bf16x2(br.k[2 * st + 1], true));
+      } else {
+        kw = make_uint4(br.k[4 * st], br.k[4 * st + 1], br.k[4 * st + 2], br.k[4 * st + 3]);
+      }
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
+    }
+    float sv[4] = {s[0] * sc, s[1] * sc, s[2] * sc, s[3] * sc};
+    uint32_t vmask = 0xfu;                                        // tokens 4c+e kept for P.V (bit e)
+    if (valid < kBlockTokens) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * c + j >= valid) sv[j] = -INFINITY;
+      vmask = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vmask |= (4 * c + e < valid) ? (1u << e) : 0u;
+    }
+    if constexpr (kCols) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * c + j >= col_valid) sv[j] = -INFINITY;
+    }
+    // ---- online softmax (base 2)
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = max_xor16(max_xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    if (__ballot(m_new > m) != 0) {
+      // a column whose max did not move keeps its scale (also when both are -inf)
+      const float alpha = kCols ? (m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f)
+                                : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < kE; ++t) acc[t] *= alpha;
+      m = m_new;
+    }
+    // a column that has seen no token yet has m = -inf and all logits -inf
+    const float mref = (kCols && m == -INFINITY) ? 0.0f : m;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    // e4m3: the block's V scale is applied in fp32 to the block's P.V product
+    // (folding it into the bf16 P would put a relative 2^-9 error on every V row)
+    const float pv = kFp8 ? 1.0f : vs;
+    const short4_t pop = __builtin_bit_cast(
+        short4_t, make_uint2(pack_bf16x2(p[0] * pv, p[1] * pv), pack_bf16x2(p[2] * pv, p[3] * pv)));
+    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n).  Masked
+    // tokens get V = 0 by selection (their slots may hold NaN).
+    uint32_t vw[4][T::kVWords];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int w = 0; w < T::kVWords; ++w) vw[e][w] = (vmask >> e & 1u) ? br.v[e][w] : 0u;
+#pragma unroll
+    for (int nn = 0; nn < kE; ++nn) {
+      uint32_t lo, hi;
+      if constexpr (kFp8) {
+        // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
+        const int w = nn / 4, byte = nn % 4;
+        const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
+        const uint32_t c01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+        const uint32_t c23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+        lo = fp8x2_to_bf16x2(c01, false);
+        hi = fp8x2_to_bf16x2(c23, false);
+      } else {
+        const int w = nn / 2;
+        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+        lo = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+        hi = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+      }
+      const short4_t vop = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+      if constexpr (kFp8) {
+        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        acc[nn] += t * vs;
+      } else {
+        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[nn], 0, 0, 0);
+      }
+    }
+  }
+
+  // The wave's total sum (the 4 lane groups hold partial sums of one head).
+  __device__ __forceinline__ float total_l() const { return sum_xor16(sum_xor32(l)); }
+
+  // Output run of this lane: d = (D/4)*c + kE*j + n  ->  o[kE*j + n].
+  __device__ __forceinline__ void unpack(float* o) const {
+#pragma unroll
+    for (int nn = 0; nn < kE; ++nn)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[kE * j + nn] = acc[nn][j];
+  }
+};
+
+// Write D/4 normalised values of one query row as bf16 (16-byte stores).
+template <int D>
+__device__ __forceinline__ void store_bf16_run(uint16_t* dst_row, int d0, const float* o, float inv) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(dst_row + d0);
+#pragma unroll
+  for (int i = 0; i < D / 8; i += 4) {
+    const uint4 w = make_uint4(pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv),
+                               pack_bf16x2(o[2 * i + 2] * inv, o[2 * i + 3] * inv),
+                               pack_bf16x2(o[2 * i + 4] * inv, o[2 * i + 5] * inv),
+                               pack_bf16x2(o[2 * i + 6] * inv, o[2 * i + 7] * inv));
+    *reinterpret_cast<uint4*>(dst + i) = w;
+  }
+}
+
+// Write D/4 unnormalised fp32 values of one workspace row.
+template <int D>
+__device__ __forceinline__ void store_f32_run(float* dst_row, int d0, const float* o) {
+  float4* dst = reinterpret_cast<float4*>(dst_row + d0);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+}  // namespace pa

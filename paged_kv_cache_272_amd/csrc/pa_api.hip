@@ -11,7 +11,6 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
-#define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace pa {
 
@@ -107,7 +106,8 @@ struct TimingRecord {
 
 struct Timing {
   std::mutex mu;
-  bool enabled = false;
+  int every = 0;            // record one decode call in `every`; 0 = off
+  int64_t seen = 0;         // decode calls since enabling
   std::vector<TimingRecord> pool;
   size_t used = 0;
 } g_timing;
@@ -116,7 +116,8 @@ constexpr size_t kMaxTimedCalls = 65536;
 
 TimingRecord* timing_slot() {
   std::lock_guard<std::mutex> lock(g_timing.mu);
-  if (!g_timing.enabled || g_timing.used >= kMaxTimedCalls) return nullptr;
+  if (g_timing.every <= 0 || g_timing.used >= kMaxTimedCalls) return nullptr;
+  if (g_timing.seen++ % g_timing.every != 0) return nullptr;
   if (g_timing.used == g_timing.pool.size()) {
     TimingRecord r{};
     if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.mid) != hipSuccess ||
@@ -162,8 +163,8 @@ PA_EXPORT int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype, v
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
   if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
-  CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens, num_kv_heads,
-                   head_dim, num_blocks, src_dtype, cache_dtype};
+  CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, nullptr, nullptr, num_tokens,
+                   num_kv_heads, head_dim, num_blocks, 0, src_dtype, cache_dtype};
   return launch_cache_write(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -191,12 +192,16 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   return bytes;
 }
 
-PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* k_cache, const void* v_cache,
-                        pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
-                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                        int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// pa_decode and pa_decode_append.  k_new/v_new non-null: appending.
+int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, const void* v_new, const void* k_cache,
+                const void* v_cache, pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const bool append = k_new != nullptr || v_new != nullptr;
   int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens);
   if (st != PA_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
@@ -208,6 +213,8 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE) return PA_ERR_BAD_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+  if (append && (!k_new || !v_new)) return PA_ERR_NULL_POINTER;
+  if (append && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_MISALIGNED;
   if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
   const WorkspaceLayout w = use_balanced(q_dtype, num_seqs, partition_tokens)
@@ -247,8 +254,18 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
   a.scale_log2 = scale * kLog2e;
   a.q_dtype = q_dtype;
   a.cache_dtype = cache_dtype;
+  // the balanced kernel writes the newest tokens itself; other paths scatter first
+  a.append = append && w.balanced ? 1 : 0;
+  a.k_new = a.append ? k_new : nullptr;
+  a.v_new = a.append ? v_new : nullptr;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (append && !a.append) {
+    CacheWriteArgs cw{k_new, v_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_scale, v_scale,
+                      nullptr, block_tables, context_lens, num_seqs, num_kv_heads, head_dim, num_blocks,
+                      max_blocks_per_seq, q_dtype, cache_dtype};
+    if (launch_cache_write(cw, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
   TimingRecord* rec = timing_slot();
   if (rec) (void)hipEventRecord(rec->start, s);
   const hipError_t e1 = w.balanced ? launch_decode_mfma_balanced(a, s) : launch_decode_partitions(a, s);
@@ -264,6 +281,32 @@ PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* 
     (void)hipEventRecord(rec->end, s);
   }
   return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT int pa_decode(void* out, const void* q, pa_dtype q_dtype, const void* k_cache, const void* v_cache,
+                        pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, q_dtype, nullptr, nullptr, k_cache, v_cache, cache_dtype, k_scale, v_scale,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+PA_EXPORT int pa_decode_append(void* out, const void* q, pa_dtype q_dtype, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, pa_dtype cache_dtype, const float* k_scale,
+                               const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL_POINTER;
+  return decode_impl(out, q, q_dtype, k_new, v_new, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, num_blocks, scale, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype, float* k_scale, float* v_scale,
@@ -282,9 +325,92 @@ PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
   return launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-PA_EXPORT int pa_timing_enable(int enable) {
+PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, const void* k_cache,
+                                const void* v_cache, pa_dtype cache_dtype, const float* k_scale,
+                                const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, float scale, const void* plan, const pa_plan_info* info,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!info) return PA_ERR_NULL_POINTER;
+  const pa_plan_info& in = *info;
+  if (in.num_seqs < 0 || in.num_q_tokens < 0 || in.num_items < 0 || in.num_columns < 0 || in.num_records < 0 ||
+      in.num_merge_rows < 0 || in.num_merge_entries < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (in.num_q_heads < 1 || in.num_kv_heads < 1 || in.num_q_heads % in.num_kv_heads) return PA_ERR_BAD_SHAPE;
+  if (in.num_q_heads / in.num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (in.head_dim != 64 && in.head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  if (q_dtype != PA_DTYPE_BF16 || cache_dtype == PA_DTYPE_F32) return PA_ERR_BAD_DTYPE;
+  const PlanLayout lay = plan_layout(in);
+  if ((int64_t)lay.bytes != in.plan_bytes) return PA_ERR_BAD_SHAPE;
+  if ((int64_t)planned_workspace_bytes(in) != in.workspace_bytes) return PA_ERR_BAD_SHAPE;
+  if (in.num_items == 0 || in.num_seqs == 0 || in.num_q_tokens == 0) return PA_OK;
+  if (in.num_columns < 1) return PA_ERR_BAD_SHAPE;
+  if (in.num_merge_rows > 0 && (in.num_records < 1 || in.num_merge_entries < 1)) return PA_ERR_BAD_SHAPE;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !plan) return PA_ERR_NULL_POINTER;
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(plan))
+    return PA_ERR_MISALIGNED;
+  const size_t ws_need = planned_workspace_bytes(in);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return PA_ERR_WORKSPACE;
+  if (ws_need > 0 && !aligned16(workspace)) return PA_ERR_MISALIGNED;
+
+  PlannedArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  const uint8_t* p = static_cast<const uint8_t*>(plan);
+  a.items = reinterpret_cast<const PlanItem*>(p + lay.items_off);
+  a.cols = reinterpret_cast<const PlanColumn*>(p + lay.cols_off);
+  a.rows = reinterpret_cast<const PlanMergeRow*>(p + lay.rows_off);
+  a.entries = reinterpret_cast<const int32_t*>(p + lay.entries_off);
+  if (ws_need > 0) {
+    const size_t rows = (size_t)in.num_records * in.num_kv_heads;
+    float* ws = static_cast<float*>(workspace);
+    a.ws_m = ws;
+    a.ws_l = ws + align_floats(rows);
+    a.ws_acc = ws + 2 * align_floats(rows);
+  }
+  a.num_items = in.num_items;
+  a.num_columns = in.num_columns;
+  a.num_records = in.num_records;
+  a.num_merge_rows = in.num_merge_rows;
+  a.num_merge_entries = in.num_merge_entries;
+  a.num_seqs = in.num_seqs;
+  a.num_q_tokens = in.num_q_tokens;
+  a.num_q_heads = in.num_q_heads;
+  a.num_kv_heads = in.num_kv_heads;
+  a.head_dim = in.head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.waves_per_wg = in.num_kv_heads < kBalancedMaxWaves ? in.num_kv_heads : kBalancedMaxWaves;
+  a.head_groups = (in.num_kv_heads + a.waves_per_wg - 1) / a.waves_per_wg;
+  a.scale_log2 = scale * kLog2e;
+  a.cache_dtype = cache_dtype;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  TimingRecord* rec = timing_slot();
+  if (rec) (void)hipEventRecord(rec->start, s);
+  if (launch_attend_planned(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (rec) (void)hipEventRecord(rec->mid, s);
+  const bool merge = in.num_merge_rows > 0;
+  if (merge && launch_attend_planned_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (rec) {
+    rec->merged = merge;
+    (void)hipEventRecord(rec->end, s);
+  }
+  return PA_OK;
+}
+
+PA_EXPORT int pa_timing_enable(int every) {
+  if (every < 0) return PA_ERR_BAD_SHAPE;
   std::lock_guard<std::mutex> lock(g_timing.mu);
-  g_timing.enabled = enable != 0;
+  g_timing.every = every;
+  g_timing.seen = 0;
   return PA_OK;
 }
 

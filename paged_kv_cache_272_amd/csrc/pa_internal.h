@@ -9,8 +9,13 @@
 
 #include "pa.h"
 
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
 namespace pa {
 
+// Slot scatter.  With slot_mapping == nullptr the slot of token t is the
+// position context_lens[t] - 1 of sequence t (its newest token), taken
+// through block_tables; sequences with no token are skipped.
 struct CacheWriteArgs {
   const void* k;
   const void* v;
@@ -19,7 +24,9 @@ struct CacheWriteArgs {
   const float* k_scale;
   const float* v_scale;
   const int64_t* slot_mapping;
-  int32_t num_tokens, num_kv_heads, head_dim, num_blocks;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_tokens, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq;
   pa_dtype src_dtype, cache_dtype;
 };
 
@@ -61,6 +68,12 @@ struct DecodeArgs {
   float* ws_l;
   float* ws_acc;
   int32_t* ws_seq_start;
+  // Appending decode: the newest token (position context_lens[b] - 1) of
+  // every sequence is taken from k_new/v_new [B, Hkv, D] (query type) and
+  // written to its slot by the wave that reads that block.
+  const void* k_new;
+  const void* v_new;
+  int32_t append;
   int32_t max_blocks_per_seq, max_context_len, num_seqs, num_q_heads, num_kv_heads;
   int32_t head_dim, num_blocks, partition_tokens, num_parts;
   int32_t balanced, num_wgs, waves_per_wg, head_groups;
@@ -95,6 +108,77 @@ constexpr int kMaxPartitionTokens = 512;
 // Workspace layout helpers (shared by size queries and launches).
 size_t workspace_section_floats(int32_t num_seqs, int32_t num_q_heads, int32_t num_parts);
 size_t align_floats(size_t n);
+
+// ---- planned attention (pa_plan_attention / pa_attend_planned)
+//
+// A packed plan is four arrays, one after the other (each 16-byte aligned):
+//   items[num_items], columns[num_columns], merge_rows[num_merge_rows],
+//   entries[num_merge_entries] (int32 record ids).
+// Item k reads logical blocks [blk_lo, blk_hi) of block-table row `seq` for
+// the `ncols` query columns columns[col0 .. col0+ncols-1]; tokens at or past
+// kv_len hold no data.  rec0 < 0: the item is the column's only
+// contribution and writes `out`; otherwise column c's partial result goes
+// to record rec0 + c.  A merge row combines the records entries[e0 .. e0+n-1]
+// into the output row of (q_row, j).  ncols == 0 marks an empty item.
+struct PlanItem {
+  int32_t seq, blk_lo, blk_hi, col0, ncols, kv_len, rec0, pad;
+};
+struct PlanColumn {
+  int32_t q_row, j, horizon, pad;   // query head = kv_head * G + j; sees positions < horizon
+};
+struct PlanMergeRow {
+  int32_t q_row, j, e0, n;
+};
+
+struct PlanLayout {
+  size_t items_off, cols_off, rows_off, entries_off, bytes;
+};
+
+inline size_t align16(size_t n) { return (n + 15) / 16 * 16; }
+
+inline PlanLayout plan_layout(const pa_plan_info& info) {
+  PlanLayout l;
+  l.items_off = 0;
+  l.cols_off = align16(l.items_off + (size_t)info.num_items * sizeof(PlanItem));
+  l.rows_off = align16(l.cols_off + (size_t)info.num_columns * sizeof(PlanColumn));
+  l.entries_off = align16(l.rows_off + (size_t)info.num_merge_rows * sizeof(PlanMergeRow));
+  l.bytes = align16(l.entries_off + (size_t)info.num_merge_entries * sizeof(int32_t));
+  return l;
+}
+
+// Records: [num_records, num_kv_heads] rows of m, l (floats) and acc[head_dim].
+inline size_t planned_workspace_bytes(const pa_plan_info& info) {
+  const size_t rows = (size_t)info.num_records * info.num_kv_heads;
+  if (rows == 0) return 0;
+  const size_t sec = (rows + 63) / 64 * 64;
+  return (2 * sec + rows * info.head_dim) * sizeof(float);
+}
+
+struct PlannedArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const PlanItem* items;
+  const PlanColumn* cols;
+  const PlanMergeRow* rows;
+  const int32_t* entries;
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
+  int32_t num_items, num_columns, num_records, num_merge_rows, num_merge_entries;
+  int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_blocks_per_seq, num_blocks;
+  int32_t waves_per_wg, head_groups;
+  float scale_log2;
+  pa_dtype cache_dtype;
+};
+
+hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream);
+hipError_t launch_attend_planned_merge(const PlannedArgs& a, hipStream_t stream);
 
 hipError_t launch_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

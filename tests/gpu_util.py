@@ -75,6 +75,14 @@ class DeviceWorkload:
                      wl.partition_tokens if partition_tokens is None else partition_tokens)
         return out
 
+    def decode_append(self, pa, partition_tokens=None, out=None):
+        wl = self.wl
+        out = self.out if out is None else out
+        pa.pa_decode_append(out, self.q, self.new_k, self.new_v, self.k_cache, self.v_cache, self.block_tables,
+                            self.context_lens, wl.max_context_len, wl.scale, self.k_scale, self.v_scale,
+                            wl.partition_tokens if partition_tokens is None else partition_tokens)
+        return out
+
 
 def oracle_after_write(wl: W.PagedWorkload):
     """Host caches after the oracle's slot scatter of the new tokens."""

@@ -99,6 +99,55 @@ def test_long_context_fp8_quantised_normals():
     _full_parity(wl, 4, True)
 
 
+def _append_parity(wl, partition_tokens=None):
+    """pa_decode_append: the newest token's slot bit-exact, nothing else in the
+    pools changed, and the output equal to the oracle's write-then-decode."""
+    log(f"append {wl.name}: B={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} kv={wl.kv_dtype} "
+        f"partition={wl.partition_tokens if partition_tokens is None else partition_tokens}")
+    dw = DeviceWorkload(wl)
+    orig_k, orig_v = dw.k_cache.clone(), dw.v_cache.clone()
+    k_ref, v_ref = oracle_after_write(wl)
+    dw.decode_append(pa, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    assert_written_rows_equal(dw, k_ref, v_ref, orig_k, orig_v)
+    err = decode_error(wl, dw.out, k_ref, v_ref, sample_seqs(wl, 32))
+    log(f"append decode max abs error {err:.3e}")
+    assert err <= TOL[wl.kv_dtype]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_append_fused(kv):
+    lens = [1, 15, 16, 17, 33, 700, 1500, 4096, 2049, 5]
+    wl = W.make_workload(name="append", seed=109, context_lens=lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         q_dtype="bf16", kv_dtype=kv, fp8_mode="values")
+    if kv == "fp8":
+        quantize_fp8_values(wl)
+    _append_parity(wl)
+
+
+def test_decode_append_many_short_sequences():
+    rng = np.random.default_rng(110)
+    lens = rng.integers(1, 70, size=600)
+    wl = W.make_workload(name="append_short", seed=111, context_lens=lens, num_q_heads=16, num_kv_heads=2,
+                         head_dim=64, q_dtype="bf16", kv_dtype="bf16")
+    _append_parity(wl)
+
+
+@pytest.mark.parametrize("kv,p", [("f32", 0), ("bf16", 256), ("fp8", 512)])
+def test_decode_append_unfused_paths(kv, p):
+    qd = "f32" if kv == "f32" else "bf16"
+    wl = W.make_workload(name="append_unfused", seed=112, context_lens=[3, 16, 17, 600, 1100], num_q_heads=8,
+                         num_kv_heads=4, head_dim=128, q_dtype=qd, kv_dtype=kv, fp8_mode="values",
+                         sigma=1.0 if kv == "f32" else 0.5)
+    if kv == "fp8":
+        quantize_fp8_values(wl)
+    _append_parity(wl, partition_tokens=p)
+
+
+def test_decode_append_full_size_8b_shape():
+    _append_parity(W.config2())
+
+
 # ---------------------------------------------------------------------------
 # edge cases and robustness
 
@@ -213,6 +262,30 @@ def test_workspace_reused_across_calls():
                      dw.context_lens[:2].contiguous(), wl.max_context_len, wl.scale, workspace=ws)
         torch.cuda.synchronize()
         assert np.abs(out_to_f64(sub) - want[:2]).max() <= TOL["bf16"]
+
+
+def test_stale_workspace_and_fewer_units_than_slices():
+    """The workspace holds garbage (NaN bytes) from before, and the batch has
+    fewer 16-token units than the split has slices, so some slices are empty:
+    no empty slice may contribute to the merge."""
+    for lens, kv, part in (([3000, 100], "bf16", 0), ([40, 33, 1000, 17], "bf16", 0), ([700, 5], "fp8", 0),
+                           ([3000, 100], "bf16", 256)):
+        wl = W.make_workload(name="stale-ws", seed=109, context_lens=lens, num_q_heads=32, num_kv_heads=8,
+                             head_dim=128, q_dtype="bf16", kv_dtype=kv)
+        quantize_fp8_values(wl)
+        dw = DeviceWorkload(wl)
+        dw.cache_write(pa)                    # the newest tokens' slots hold NaN until written
+        k_ref, v_ref = oracle_after_write(wl)
+        need = pa.pa_decode_workspace_size(len(lens), 32, 8, 128, wl.max_context_len, part)
+        assert need > 0
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+        log(f"stale workspace lens={lens} kv={kv} partition_tokens={part}")
+        out = torch.empty_like(dw.q)
+        pa.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, wl.max_context_len,
+                     wl.scale, dw.k_scale, dw.v_scale, part, workspace=ws)
+        torch.cuda.synchronize()
+        err = decode_error(wl, out, k_ref, v_ref, list(range(len(lens))))
+        assert err <= TOL[kv], (lens, kv, part, err)
 
 
 def test_bitwise_repeatable():

@@ -1,0 +1,165 @@
+"""GPU parity of planned attention (pa_plan_attention + pa_attend_planned)
+against the CPU oracle: several new tokens per sequence (oracle.multi_query_ref)
+and prefix blocks shared between sequences (oracle.decode_ref)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pa_workloads as W
+from gpu_util import TOL, DeviceWorkload, log, oracle_after_write, out_to_f64, quantize_fp8_values, to_dev
+
+pytestmark = pytest.mark.gpu
+pa = pytest.importorskip("paged_kv_cache_272_amd")
+
+
+def _run(dw, wl, share=False, target=0, workspace=None, tables=None):
+    """tables: (host, device) block tables to use instead of the workload's."""
+    tables_host, tables_dev = (wl.block_tables, dw.block_tables) if tables is None else tables
+    plan, info = pa.pa_plan_attention(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                      q_start=wl.q_start, block_tables=tables_host if share else None,
+                                      share_prefix=share, target_items=target)
+    out = torch.empty_like(dw.q)
+    pa.pa_attend_planned(out, dw.q, dw.k_cache, dw.v_cache, tables_dev, wl.scale, pa.plan_to_device(plan),
+                         info, dw.k_scale, dw.v_scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, info
+
+
+def _multi_query_case(name, seed, ctxs, q_lens, hq, hkv, d, kv, fp8_mode="values"):
+    wl = W.make_multi_query_workload(name=name, seed=seed, context_lens=ctxs, q_lens=q_lens, num_q_heads=hq,
+                                     num_kv_heads=hkv, head_dim=d, kv_dtype=kv, fp8_mode=fp8_mode)
+    quantize_fp8_values(wl)
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    want = oracle.multi_query_ref(wl.q, wl.q_start, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale,
+                                  "bf16", kv, wl.k_scale, wl.v_scale)
+    return wl, dw, want
+
+
+@pytest.mark.parametrize("hq,hkv,d,kv", [(32, 8, 128, "bf16"), (64, 8, 128, "bf16"), (8, 8, 64, "bf16"),
+                                         (16, 1, 64, "bf16"), (32, 8, 128, "fp8"), (64, 8, 128, "fp8")])
+def test_multi_query_parity(hq, hkv, d, kv):
+    ctxs = [40, 7, 100, 16, 33, 300, 1, 520]
+    q_lens = [5, 7, 0, 16, 1, 37, 1, 4]
+    wl, dw, want = _multi_query_case("mq", 201, ctxs, q_lens, hq, hkv, d, kv)
+    for target in (0, 5, 3000):
+        log(f"multi-query hq={hq} hkv={hkv} d={d} kv={kv} target_items={target}")
+        out, info = _run(dw, wl, target=target)
+        err = float(np.abs(out_to_f64(out) - want).max())
+        log(f"  items={info.num_items} records={info.num_records} max abs error {err:.3e}")
+        assert np.isfinite(out_to_f64(out)).all()
+        assert err <= TOL[kv], err
+
+
+def test_draft_verification_8b_shape():
+    """Four draft tokens per sequence on the 8B-shaped batch (64 sequences, contexts 128..4096)."""
+    base = W.config2(with_values=False)
+    ctxs = [int(c) for c in base.context_lens]
+    wl = W.make_multi_query_workload(name="verify4", seed=202, context_lens=ctxs, q_lens=[4] * len(ctxs),
+                                     num_q_heads=32, num_kv_heads=8, head_dim=128)
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    seqs = [0, 5, 17, 31, 40, 63]
+    want = oracle.multi_query_ref(wl.q, wl.q_start, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale,
+                                  "bf16", "bf16", seqs=seqs)
+    out, info = _run(dw, wl)
+    got = out_to_f64(out)
+    rows = np.concatenate([np.arange(wl.q_start[b], wl.q_start[b + 1]) for b in seqs])
+    err = float(np.abs(got[rows] - want[rows]).max())
+    log(f"verify4: items={info.num_items} max abs error {err:.3e} over {len(seqs)} sequences")
+    assert err <= TOL["bf16"]
+
+
+def test_chunked_prefill_chunk():
+    """A 256-token chunk appended to 768 cached tokens (and a whole 300-token prompt)."""
+    wl, dw, want = _multi_query_case("chunk", 203, [1024, 300], [256, 300], 32, 8, 128, "bf16")
+    out, info = _run(dw, wl)
+    err = float(np.abs(out_to_f64(out) - want).max())
+    log(f"chunked prefill: items={info.num_items} max abs error {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_decode_through_a_plan_matches_oracle():
+    wl = W.make_workload(name="plan-decode", seed=204, context_lens=[1, 17, 600, 1500, 33], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    want = oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16")
+    for target in (0, 7):
+        out, _ = _run(dw, wl, target=target)
+        assert np.abs(out_to_f64(out) - want).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_shared_prefix_decode_parity(kv):
+    """Parallel sampling (the 32 prompts x 8 samples layout): prefix blocks read once
+    per prompt, with the tables before copy-on-write (125 shared blocks) and after it."""
+    wl = W.config4() if kv == "bf16" else W.make_shared_prefix_workload(
+        name="share-fp8", seed=205, num_prompts=8, samples_per_prompt=4, prefix_tokens=512, suffix_max=200,
+        num_q_heads=32, num_kv_heads=8, head_dim=128)
+    if kv == "fp8":
+        # e4m3 pool: the bf16 pool's values with per-(block, head) scales from each block's amax
+        vals_k, vals_v = oracle.bf16_to_f32(wl.k_cache), oracle.bf16_to_f32(wl.v_cache)
+        wl.k_scale = (np.maximum(np.nan_to_num(np.abs(vals_k)).max(axis=(2, 3)), 1e-3) / 448).astype(np.float32)
+        wl.v_scale = (np.maximum(np.nan_to_num(np.abs(vals_v)).max(axis=(2, 3)), 1e-3) / 448).astype(np.float32)
+        wl.k_cache = oracle.quantize_pool_ref(vals_k, wl.k_scale)
+        wl.v_cache = oracle.quantize_pool_ref(vals_v, wl.v_scale)
+        wl.kv_dtype = "fp8"
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    ks, vs = wl.k_scale, wl.v_scale
+    seqs = sorted({0, 1, 7, 8, 100, wl.num_seqs - 1} & set(range(wl.num_seqs)))
+    for which in ("shared", "copied"):
+        if which == "copied":
+            pa.pa_copy_blocks(dw.k_cache, dw.v_cache, to_dev(wl.copy_pairs.astype(np.int32), "i32"), dw.k_scale,
+                              dw.v_scale)
+            k_ref, v_ref, ks, vs = oracle.copy_blocks_ref(k_ref, v_ref, wl.copy_pairs, ks, vs)
+            host = wl.block_tables
+        else:
+            host = wl.block_tables_shared
+        tables = (host, to_dev(host.astype(np.int32), "i32"))
+        want = oracle.decode_ref(wl.q, k_ref, v_ref, host, wl.context_lens, wl.scale, "bf16", wl.kv_dtype, ks, vs,
+                                 seqs=seqs)
+        out, info = _run(dw, wl, share=True, tables=tables)
+        err = float(np.abs(out_to_f64(out)[seqs] - want).max())
+        log(f"shared prefix {kv} {which}: groups={info.num_shared_groups} items={info.num_items} "
+            f"block reads={info.block_reads} max abs error {err:.3e}")
+        assert info.num_shared_groups > 0
+        assert err <= TOL[kv]
+        plain, _ = _run(dw, wl, share=False, tables=tables)
+        assert np.abs(out_to_f64(plain)[seqs] - want).max() <= TOL[kv]
+
+
+def test_planned_stale_workspace():
+    wl, dw, want = _multi_query_case("mq-stale", 206, [300, 40], [20, 40], 32, 8, 128, "bf16")
+    plan, info = pa.pa_plan_attention(wl.context_lens, 32, 8, 128, q_start=wl.q_start, target_items=9)
+    assert info.workspace_bytes > 0
+    ws = torch.full((info.workspace_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dw.q)
+    pa.pa_attend_planned(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, wl.scale, pa.plan_to_device(plan),
+                         info, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.abs(out_to_f64(out) - want).max() <= TOL["bf16"]
+
+
+def test_planned_rejects_bad_calls_and_empty_plan():
+    wl, dw, _ = _multi_query_case("mq-err", 207, [40], [3], 8, 2, 64, "bf16")
+    plan, info = pa.pa_plan_attention(wl.context_lens, 8, 2, 64, q_start=wl.q_start)
+    dplan = pa.plan_to_device(plan)
+    out = torch.empty_like(dw.q)
+    bad = pa.PlanInfo.from_buffer_copy(info)
+    bad.plan_bytes += 16
+    with pytest.raises(pa.PaError):
+        pa.pa_attend_planned(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, wl.scale, dplan, bad)
+    f32q = torch.zeros(dw.q.shape, dtype=torch.float32, device="cuda")
+    with pytest.raises(pa.PaError):
+        pa.pa_attend_planned(f32q, f32q, dw.k_cache, dw.v_cache, dw.block_tables, wl.scale, dplan, info)
+    eplan, einfo = pa.pa_plan_attention(np.zeros(0, dtype=np.int32), 8, 2, 64)
+    e = torch.empty(0, 8, 64, dtype=torch.bfloat16, device="cuda")
+    pa.pa_attend_planned(e, e, dw.k_cache, dw.v_cache, dw.block_tables, wl.scale, pa.plan_to_device(eplan), einfo)
+    torch.cuda.synchronize()
