@@ -1,21 +1,32 @@
 #!/usr/bin/env python3
-"""Paged-KV decode benchmark on one MI355X.
+"""Paged-KV attention benchmark on one MI355X.
 
-One step = one decode step of the Llama-3-8B-shaped layer (64 sequences,
-32 query / 8 KV heads, head_dim 128, bf16, contexts U{128..4096}): each
-sequence's new token is written into its slot and the paged decode runs
-over the cache including it.  By default this is one pa_decode_append call
-(the decode kernel writes the new rows itself, then the log-sum-exp merge
-kernel runs); `--step separate` times pa_cache_write + pa_decode instead.  Inputs are seeded,
-synthetic and resident in HBM before timing; the K/V pool is rotated over
-several copies so the 256 MB Infinity Cache cannot hold it between steps.
+Default workload (decode_8b, the headline): one step = one decode step of
+the Llama-3-8B-shaped layer (64 sequences, 32 query / 8 KV heads,
+head_dim 128, bf16, contexts U{128..4096}): each sequence's new token is
+written into its slot and the paged decode runs over the cache including
+it.  By default this is one pa_decode_append call (the decode kernel writes
+the new rows itself, then the log-sum-exp merge kernel runs); `--step
+separate` times pa_cache_write + pa_decode instead.
 
-Prints one JSON line: whole-step KV throughput (algorithmic bytes / step
-time), sequences/s, fraction of the 8 TB/s HBM spec and of a measured
-stream-read ceiling, the decode partition kernel's roofline entry (its
-algorithmic bytes over its average duration, from HIP events recorded on
-its own stream during the timed steps), and the CPU oracle timed on a
-bounded sample of the same workload.
+Other workloads (--workload): decode_70b (256 sequences, GQA-8, lognormal
+contexts), long_ctx_fp8 (8 x 131072 tokens, e4m3 KV), shared_prefix_32x8
+(32 prompts x 8 samples sharing a 2000-token prefix: slot write + planned
+attention reading each shared block once), verify4_8b (4 draft tokens per
+sequence on the 8B batch) and chunked_prefill (4 chunks of 512 tokens
+appended to 3584 cached tokens).
+
+Inputs are seeded, synthetic and resident in HBM before timing; the K/V
+pool is rotated over several copies so the 256 MB Infinity Cache cannot
+hold it between steps.
+
+Prints one JSON line: whole-step throughput (algorithmic bytes / step
+time; for shared prefixes every physical block counts once), sequences/s,
+fraction of the 8 TB/s HBM spec and of a measured stream-read ceiling, the
+dominant kernel's roofline entry (its algorithmic bytes, or flops for the
+prefill chunk, over its average duration from HIP events recorded on its
+own stream during the timed steps), and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,13 +43,22 @@ sys.path.insert(0, ROOT)
 
 SPEC_HBM_GBPS = 8000.0
 METRIC = "paged-decode KV GB/s & % of MI355X HBM peak; seqs/s (8B-shape, bs=64)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_bs64.json")
-KERNEL_SOURCES = ["decode_valu.hip", "decode_mfma.hip", "pa_api.hip", "pa_device.h", "pa_internal.h"]
+DECODE_SOURCES = ["decode_mfma.hip", "mfma_tile.h", "pa_device.h", "pa_internal.h"]
+PLANNED_SOURCES = ["attend_planned.hip", "mfma_tile.h", "pa_device.h", "pa_internal.h"]
+# workload -> (dominant kernel's name, the sources it is built from)
+KERNELS = {
+    "decode_8b": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
+    "decode_70b": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
+    "long_ctx_fp8": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
+    "shared_prefix_32x8": ("attend_planned_kernel", PLANNED_SOURCES),
+    "verify4_8b": ("attend_planned_kernel", PLANNED_SOURCES),
+    "chunked_prefill": ("attend_planned_kernel", PLANNED_SOURCES),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         p = os.path.join(ROOT, "paged_kv_cache_272_amd", "csrc", name)
         if os.path.exists(p):
             h.update(name.encode())
@@ -51,6 +71,9 @@ def parse_args():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) into the "
                          "HBM-traffic record the roofline entry reports, and exit")
+    ap.add_argument("--workload", choices=sorted(KERNELS), default="decode_8b",
+                    help="decode_8b (default) is the headline step; the others measure the other shapes and "
+                         "the planned (multi-token, shared-prefix) paths")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -83,7 +106,6 @@ def measured_stream_read(pa, torch, nbytes=4 << 30, reps=5):
 
 
 COPY_PROBE_BYTES = 1 << 30
-DECODE_KERNEL = "decode_mfma_balanced_kernel"
 COPY_KERNEL = "probe_copy_kernel"
 
 
@@ -110,7 +132,7 @@ def _counter_per_dispatch(run_dir, counter):
     return out
 
 
-def traffic_record(fetch_dir, write_dir):
+def traffic_record(workload, fetch_dir, write_dir):
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
 
@@ -124,10 +146,12 @@ def traffic_record(fetch_dir, write_dir):
     copy_read, copy_write = pick(fetch, COPY_KERNEL), pick(write, COPY_KERNEL)
     read_scale = COPY_PROBE_BYTES / copy_read
     write_scale = COPY_PROBE_BYTES / copy_write
-    dec_read, dec_write = pick(fetch, DECODE_KERNEL), pick(write, DECODE_KERNEL)
+    kernel, sources = KERNELS[workload]
+    dec_read, dec_write = pick(fetch, kernel), pick(write, kernel)
     rec = {
-        "kernel": DECODE_KERNEL,
-        "kernel_source_hash": kernel_source_hash(),
+        "workload": workload,
+        "kernel": kernel,
+        "kernel_source_hash": kernel_source_hash(sources),
         "fetch_bytes_per_launch_raw": dec_read, "write_bytes_per_launch_raw": dec_write,
         "copy_probe_bytes": COPY_PROBE_BYTES, "copy_probe_fetch_raw": copy_read, "copy_probe_write_raw": copy_write,
         "read_scale": read_scale, "write_scale": write_scale,
@@ -136,27 +160,25 @@ def traffic_record(fetch_dir, write_dir):
                   "per-dispatch value, each scaled by (known bytes / counter) of a 1 GiB probe copy in the "
                   "same run",
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def cpu_baseline(wl, k_ref, v_ref, budget_s):
-    import numpy as np
-    import oracle
+def cpu_baseline(bench, budget_s):
+    """The oracle on a bounded sample of the same workload: whole sequences,
+    cycling over the batch, single-threaded BLAS, until the time budget ends."""
     from threadpoolctl import threadpool_limits
+    bench.cpu_prepare()
     with threadpool_limits(limits=1):
-        done, t_start = [], time.perf_counter()
-        while time.perf_counter() - t_start < budget_s:       # whole passes over the batch, as time allows
-            for b in range(wl.num_seqs):
-                oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16",
-                                  "bf16", seqs=[b])
-                done.append(b)
+        done, nbytes, t_start = 0, 0, time.perf_counter()
+        while time.perf_counter() - t_start < budget_s:
+            for b in range(bench.num_seqs):
+                nbytes += bench.cpu_one(b)
+                done += 1
                 if time.perf_counter() - t_start >= budget_s:
                     break
         elapsed = time.perf_counter() - t_start
-    lens = wl.context_lens[done]
-    nbytes = oracle.decode_algorithmic_bytes(lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2, 2, 2)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -167,75 +189,217 @@ def cpu_baseline(wl, k_ref, v_ref, budget_s):
         pass
     return {
         "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"float64 numpy oracle (decode_ref), BLAS limited to 1 thread, {len(done)} sequence decodes "
-                  f"cycling over the {wl.num_seqs}-sequence batch ({int(lens.sum())} tokens, "
-                  f"{nbytes / 1e6:.1f} MB algorithmic) in {elapsed:.1f} s; host CPU {cpu}",
-        "seqs_per_s": round(len(done) / elapsed, 3),
+        "sample": f"float64 numpy oracle ({bench.cpu_kind}), BLAS limited to 1 thread, {done} sequences cycling "
+                  f"over the {bench.num_seqs}-sequence batch ({nbytes / 1e6:.1f} MB algorithmic) in {elapsed:.1f} s; "
+                  f"host CPU {cpu}",
+        "seqs_per_s": round(done / elapsed, 3),
     }
+
+
+class Bench:
+    """One workload: prepared calls per pool, byte and flop counts, labels."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def _dev(torch, np, a, kind=None):
+    a = np.ascontiguousarray(a)
+    if kind == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def build_decode(args, pa, torch, np, W, oracle, name):
+    """Decode workloads: one new token per sequence (pa_decode_append, or
+    pa_cache_write + pa_decode with --step separate)."""
+    wl = {"decode_8b": W.config2, "decode_70b": W.config3, "long_ctx_fp8": W.config5}[name]()
+    kv = wl.kv_dtype
+    q = _dev(torch, np, wl.q, "bf16")
+    new_k, new_v = _dev(torch, np, wl.new_k, "bf16"), _dev(torch, np, wl.new_v, "bf16")
+    bt, cl, slots = _dev(torch, np, wl.block_tables), _dev(torch, np, wl.context_lens), _dev(torch, np, wl.slot_mapping)
+    k0, v0 = _dev(torch, np, wl.k_cache, kv if kv == "bf16" else None), _dev(torch, np, wl.v_cache,
+                                                                            kv if kv == "bf16" else None)
+    ks = None if wl.k_scale is None else _dev(torch, np, wl.k_scale)
+    vs = None if wl.v_scale is None else _dev(torch, np, wl.v_scale)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
+    out = torch.empty_like(q)
+    ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                           wl.max_context_len, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    steps = []
+    for kc, vc in pools:
+        if args.step == "append":
+            steps.append((pa.prepare_decode_append(out, q, new_k, new_v, kc, vc, bt, cl, wl.max_context_len,
+                                                   wl.scale, ks, vs, partition_tokens=args.partition_tokens,
+                                                   workspace=ws),))
+        else:
+            steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots, ks, vs),
+                          pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale, ks, vs,
+                                            partition_tokens=args.partition_tokens, workspace=ws)))
+    eb = 1 if kv == "fp8" else 2
+    decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                   eb, 2, 2, fp8_scales=kv == "fp8")
+    write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * (2 + eb) * 2 + wl.num_seqs * 8
+    part = pa.pa_decode_partition_tokens(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_context_len, args.partition_tokens)
+    labels = {"decode_8b": ("llama3_8b_shape_decode_bs64", "U{128..4096}"),
+              "decode_70b": ("llama3_70b_shape_decode_bs256", "lognormal median 2048 in [16, 8192]"),
+              "long_ctx_fp8": ("llama3_70b_shape_fp8_decode_bs8_ctx131072", "131072 each")}[name]
+    k_ref = v_ref = None
+
+    def cpu_prepare():
+        nonlocal k_ref, v_ref
+        k_ref, v_ref = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping,
+                                              "bf16", kv, wl.k_scale, wl.v_scale)
+
+    def cpu_one(b):
+        oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
+                          wl.k_scale, wl.v_scale, seqs=[b])
+        return oracle.decode_algorithmic_bytes(wl.context_lens[b:b + 1], wl.num_q_heads, wl.num_kv_heads,
+                                               wl.head_dim, eb, 2, 2, fp8_scales=kv == "fp8")
+
+    return Bench(
+        workload=labels[0], steps=steps, pools=len(pools), step_bytes=decode_bytes + write_bytes,
+        kernel_bytes=decode_bytes, kernel_flops=None, num_seqs=wl.num_seqs, dtype="bf16" if kv == "bf16" else "fp8",
+        kernel_label="decode partition kernel",
+        data=("synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)" if kv == "bf16" else
+              "synthetic (seeded bf16 q, random finite e4m3 codes with per-(block, head) scales 2^U(-8,-6))"),
+        config={"workload": labels[0], "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                "head_dim": wl.head_dim, "block_size": 16, "context_lens": labels[1],
+                "sum_context": int(wl.context_lens.sum()), "kv_dtype": kv, "pool_blocks": wl.num_blocks,
+                "pools_rotated": len(pools),
+                "work_split": ("balanced slices of the (sequence, block) list" if args.partition_tokens == 0
+                               else f"{part}-token partitions"),
+                "step": (f"pa_decode_append: slot write of the {wl.num_seqs} new tokens fused into the decode"
+                         if args.step == "append" else f"pa_cache_write({wl.num_seqs} tokens) + pa_decode")},
+        cpu_prepare=cpu_prepare, cpu_one=cpu_one, cpu_kind="decode_ref")
+
+
+def build_planned(args, pa, torch, np, W, oracle, name):
+    """Planned attention workloads (host plan built once before timing; its
+    build time is reported): the 32 x 8 shared-prefix decode (slot write of
+    the new tokens + prefix-shared attention), draft verification of 4
+    tokens per sequence on the 8B batch, and a chunked-prefill chunk."""
+    share = name == "shared_prefix_32x8"
+    if share:
+        wl = W.config4()
+        tables_host = wl.block_tables
+    elif name == "verify4_8b":
+        base = W.config2(with_values=False)
+        wl = W.make_multi_query_workload(name=name, seed=302, context_lens=[int(c) for c in base.context_lens],
+                                         q_lens=[4] * base.num_seqs, num_q_heads=32, num_kv_heads=8, head_dim=128)
+        tables_host = wl.block_tables
+    else:
+        wl = W.make_multi_query_workload(name=name, seed=303, context_lens=[4096] * 4, q_lens=[512] * 4,
+                                         num_q_heads=32, num_kv_heads=8, head_dim=128)
+        tables_host = wl.block_tables
+    q = _dev(torch, np, wl.q, "bf16")
+    new_k, new_v = _dev(torch, np, wl.new_k, "bf16"), _dev(torch, np, wl.new_v, "bf16")
+    bt, slots = _dev(torch, np, wl.block_tables), _dev(torch, np, wl.slot_mapping)
+    k0, v0 = _dev(torch, np, wl.k_cache, "bf16"), _dev(torch, np, wl.v_cache, "bf16")
+    if share:
+        pairs = _dev(torch, np, wl.copy_pairs.astype(np.int32))
+        pa.pa_copy_blocks(k0, v0, pairs)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
+    t_plan = time.perf_counter()
+    for _ in range(5):
+        plan, info = pa.pa_plan_attention(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                          q_start=wl.q_start, block_tables=tables_host if share else None,
+                                          share_prefix=share)
+    plan_ms = (time.perf_counter() - t_plan) / 5 * 1e3
+    dplan = pa.plan_to_device(plan)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(info.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    steps = []
+    for kc, vc in pools:
+        call = pa.prepare_attend_planned(out, q, kc, vc, bt, wl.scale, dplan, info, workspace=ws)
+        steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots), call) if share else (call,))
+    q_rows = int(wl.q.shape[0])
+    kernel_bytes = oracle.physical_kv_bytes(wl.block_tables, wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                                            wl.head_dim, 2, q_rows)
+    logical_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                    2, 2, 2)
+    write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * 2 * 2 * 2 + wl.num_seqs * 8 if share else 0
+    qs = wl.q_start if wl.q_start is not None else np.arange(wl.num_seqs + 1)
+    horizons = np.concatenate([np.arange(int(c) - (qs[b + 1] - qs[b]) + 1, int(c) + 1)
+                               for b, c in enumerate(wl.context_lens)])
+    flops = 4 * wl.head_dim * wl.num_q_heads * int(horizons.sum())
+    label = {"shared_prefix_32x8": "shared_prefix_32x8_decode", "verify4_8b": "llama3_8b_shape_verify4_bs64",
+             "chunked_prefill": "llama3_8b_shape_prefill_chunk512_ctx4096_x4"}[name]
+    k_ref = v_ref = None
+
+    def cpu_prepare():
+        nonlocal k_ref, v_ref
+        k_ref, v_ref = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping,
+                                              "bf16", "bf16")
+        if share:
+            k_ref, v_ref, _, _ = oracle.copy_blocks_ref(k_ref, v_ref, wl.copy_pairs)
+
+    def cpu_one(b):
+        if share:
+            oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16",
+                              seqs=[b])
+        else:
+            oracle.multi_query_ref(wl.q, wl.q_start, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale,
+                                   "bf16", "bf16", seqs=[b])
+        return oracle.physical_kv_bytes(wl.block_tables[b:b + 1], wl.context_lens[b:b + 1], wl.num_q_heads,
+                                        wl.num_kv_heads, wl.head_dim, 2, int(qs[b + 1] - qs[b]))
+
+    config = {"workload": label, "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "block_size": 16, "query_tokens": q_rows,
+              "sum_context": int(wl.context_lens.sum()), "kv_dtype": "bf16", "pool_blocks": wl.num_blocks,
+              "pools_rotated": len(pools), "plan": info.as_dict(), "plan_build_ms_host": round(plan_ms, 3),
+              "logical_kv_bytes": int(logical_bytes),
+              "step": ("pa_cache_write(256 tokens) + pa_attend_planned with prefix sharing (plan built on the host "
+                       "before timing)" if share else
+                       "pa_attend_planned over caches already holding the new tokens' K/V (plan built before timing)")}
+    return Bench(
+        workload=label, steps=steps, pools=len(pools), step_bytes=kernel_bytes + write_bytes,
+        kernel_bytes=kernel_bytes, kernel_flops=flops, num_seqs=wl.num_seqs, dtype="bf16",
+        kernel_label="planned attention kernel",
+        data="synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)", config=config,
+        logical_bytes=logical_bytes, cpu_prepare=cpu_prepare, cpu_one=cpu_one,
+        cpu_kind="decode_ref" if share else "multi_query_ref", mfma_bound=name == "chunked_prefill")
+
+
+WORKLOADS = {"decode_8b": build_decode, "decode_70b": build_decode, "long_ctx_fp8": build_decode,
+             "shared_prefix_32x8": build_planned, "verify4_8b": build_planned, "chunked_prefill": build_planned}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def main():
     args = parse_args()
     if args.traffic_from:
-        traffic_record(*args.traffic_from)
+        traffic_record(args.workload, *args.traffic_from)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the decode shards by sequence or KV head with no exchange; see the design notes). "
+              "(the decode shards by sequence or KV head with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
     import torch
 
+    import oracle
     import paged_kv_cache_272_amd as pa
     import pa_workloads as W
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    wl = W.config2()
-    gen_s = time.perf_counter() - t_gen
-    print(f"# workload generated in {gen_s:.1f} s: {wl.num_blocks} blocks, sum ctx {int(wl.context_lens.sum())}",
-          file=sys.stderr, flush=True)
-
-    def dev(a, bf16=False):
-        a = np.ascontiguousarray(a)
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
-        return t.to("cuda")
-
-    q = dev(wl.q, True)
-    new_k, new_v = dev(wl.new_k, True), dev(wl.new_v, True)
-    bt, cl, slots = dev(wl.block_tables), dev(wl.context_lens), dev(wl.slot_mapping)
-    k0, v0 = dev(wl.k_cache, True), dev(wl.v_cache, True)
-    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
-    out = torch.empty_like(q)
-    part = pa.pa_decode_partition_tokens(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                         wl.max_context_len, args.partition_tokens)
-    ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                           wl.max_context_len, args.partition_tokens)
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    steps = []
-    for kc, vc in pools:
-        if args.step == "append":
-            steps.append((pa.prepare_decode_append(out, q, new_k, new_v, kc, vc, bt, cl, wl.max_context_len,
-                                                   wl.scale, partition_tokens=args.partition_tokens,
-                                                   workspace=ws),))
-        else:
-            steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots),
-                          pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale,
-                                            partition_tokens=args.partition_tokens, workspace=ws)))
-
-    import oracle
-    decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
-                                                   wl.head_dim, 2, 2, 2)
-    write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * 2 * 2 * 2 + wl.num_seqs * 8
-    step_bytes = decode_bytes + write_bytes
+    bench = WORKLOADS[args.workload](args, pa, torch, np, W, oracle, args.workload)
+    print(f"# {bench.workload}: set up in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     copy_probe(pa, torch)
     peak_meas = measured_stream_read(pa, torch)
     print(f"# measured stream read {peak_meas:.0f} GB/s", file=sys.stderr, flush=True)
 
+    steps = bench.steps
     for i in range(args.warmup):
         for call in steps[i % len(steps)]:
             call()
@@ -254,17 +418,29 @@ def main():
     part_ms, merge_ms, calls = pa.pa_timing_read()
 
     step_s = (t1 - t0) / args.steps
-    value = step_bytes / step_s / 1e9
+    value = bench.step_bytes / step_s / 1e9
     part_avg_ms = part_ms / max(calls, 1)
     merge_avg_ms = merge_ms / max(calls, 1)
-    achieved = decode_bytes / (part_avg_ms * 1e-3) / 1e9
+    achieved = bench.kernel_bytes / (part_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("kernel_source_hash") == kernel_source_hash():
+    tf = traffic_file(args.workload)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("kernel_source_hash") == kernel_source_hash(KERNELS[args.workload][1]):
             traffic = rec.get("hbm_bytes_per_launch")
 
+    roofline = {
+        "kernel": bench.kernel_label,
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": SPEC_HBM_GBPS, "unit": "GB/s",
+        "frac": round(achieved / SPEC_HBM_GBPS, 4), "traffic": traffic,
+        "algorithmic_bytes_per_launch": int(bench.kernel_bytes),
+    }
+    if getattr(bench, "mfma_bound", False):
+        tflops = bench.kernel_flops / (part_avg_ms * 1e-3) / 1e12
+        roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tflops / 2500.0, 4), "algorithmic_flops_per_launch": int(bench.kernel_flops),
+                         "kv_GBps": round(achieved, 1)})
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -276,39 +452,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)",
-        "config": {
-            "workload": "llama3_8b_shape_decode_bs64",
-            "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
-            "head_dim": wl.head_dim, "block_size": 16, "context_lens": "U{128..4096}",
-            "sum_context": int(wl.context_lens.sum()), "kv_dtype": "bf16", "pool_blocks": wl.num_blocks,
-            "pools_rotated": len(pools),
-            "work_split": ("balanced slices of the (sequence, block) list" if args.partition_tokens == 0
-                           else f"{part}-token partitions"),
-            "step": ("pa_decode_append: slot write of the 64 new tokens fused into the decode"
-                     if args.step == "append" else "pa_cache_write(64 tokens) + pa_decode"),
-        },
-        "seqs_per_s": round(wl.num_seqs / step_s, 1),
+        "dtype": bench.dtype,
+        "data": bench.data,
+        "config": bench.config,
+        "seqs_per_s": round(bench.num_seqs / step_s, 1),
         "pct_of_spec_hbm": round(100 * value / SPEC_HBM_GBPS, 2),
         "measured_stream_read_GBps": round(peak_meas, 1),
         "pct_of_measured_stream_read": round(100 * value / peak_meas, 2),
-        "step_algorithmic_bytes": int(step_bytes),
+        "step_algorithmic_bytes": int(bench.step_bytes),
         "decode_partition_kernel_ms": round(part_avg_ms, 5),
         "decode_merge_kernel_ms": round(merge_avg_ms, 5),
-        "kernel_timing": f"HIP events on the decode stream around {calls} of the {args.steps} timed steps",
-        "roofline": {
-            "kernel": "decode partition kernel",
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": SPEC_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / SPEC_HBM_GBPS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(decode_bytes),
-        },
+        "kernel_timing": f"HIP events on the compute stream around {calls} of the {args.steps} timed steps",
+        "roofline": roofline,
         "host": platform.node(),
     }
+    if getattr(bench, "logical_bytes", None):
+        result["logical_GBps"] = round(bench.logical_bytes / step_s / 1e9, 1)
     if not args.no_cpu_baseline:
-        k_ref, v_ref = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping,
-                                              "bf16", "bf16")
-        result["cpu_baseline"] = cpu_baseline(wl, k_ref, v_ref, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

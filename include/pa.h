@@ -229,7 +229,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
  * shared prefix is stored once and referenced by every sharer; "推理优化"
  * section 一, prefix caching).  With PA_PLAN_SHARE_PREFIX the plan reads
  * such a run of blocks once for all sharers (their query columns side by
- * side in one MFMA tile) and merges that partial result with each sharer's
+ * side in the MFMA tiles of one wave) and merges that partial result with each sharer's
  * own suffix by log-sum-exp; the result equals the unshared computation.
  *
  * The work is described by a plan built on the host from host copies of
@@ -240,12 +240,14 @@ int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
 
 typedef struct pa_plan_info {
   int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
-  int32_t num_items;          /* work items (tile of <= 16 query columns, run of blocks), padded */
+  int32_t num_items;          /* work items: (<= 32 query columns, run of blocks) */
   int32_t num_columns;        /* query columns: (new token, query head within its group) */
   int32_t num_records;        /* partial results, each [num_kv_heads] x (m, l, acc[head_dim]) */
   int32_t num_merge_rows;     /* columns whose result is merged from partial results */
   int32_t num_merge_entries;
   int32_t num_shared_groups;  /* runs of prefix blocks read once for several sequences */
+  int32_t num_wgs;            /* workgroups (equal slices of the work) per KV-head group */
+  int32_t max_item_columns;   /* most query columns of one item (<= 32) */
   int32_t reserved;
   int64_t plan_bytes;         /* size of the packed plan */
   int64_t workspace_bytes;    /* scratch pa_attend_planned needs (0: none) */
@@ -261,8 +263,9 @@ typedef struct pa_plan_info {
  * (q_start[b] = b, the decode case).  context_lens [num_seqs] count every
  * token of the sequence including the new ones.  block_tables
  * [num_seqs, max_blocks_per_seq] is read only with PA_PLAN_SHARE_PREFIX
- * (NULL allowed otherwise).  target_items: how many work items to cut the
- * work into (0 = automatic).  `plan` receives info->plan_bytes bytes; pass
+ * (NULL allowed otherwise).  target_slices: how many equal slices
+ * (workgroups) to cut the work into (0 = automatic: about 2048 waves over
+ * the device; never more slices than 16-token blocks to read).  `plan` receives info->plan_bytes bytes; pass
  * plan = NULL to learn the sizes only.  Errors: NULL_POINTER, BAD_SHAPE
  * (inconsistent lengths, context past the block table), UNSUPPORTED
  * (group > 16, head_dim not 64/128), WORKSPACE (plan_capacity too small).
@@ -271,7 +274,7 @@ typedef struct pa_plan_info {
 int pa_plan_attention(const int32_t* q_start, const int32_t* context_lens,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t flags, int32_t target_items,
+                      int32_t head_dim, int32_t flags, int32_t target_slices,
                       void* plan, size_t plan_capacity, pa_plan_info* info);
 
 /*

@@ -10,12 +10,12 @@ from .formats import (E4M3_MAX, bf16_to_f32, bf16_to_f64, e4m3_encode, e4m3_quan
                       e4m3_to_f64, e4m3_value)
 from .paged_attention import (attend, decode_partitioned_ref, decode_ref, gather_kv, lse_merge_ref,
                               multi_query_ref, partition_stats, to_f64)
-from .sizes import decode_algorithmic_bytes, internal_waste_tokens, kv_bytes, pages_for
+from .sizes import decode_algorithmic_bytes, internal_waste_tokens, kv_bytes, pages_for, physical_kv_bytes
 
 __all__ = [
     "cache_write_ref", "copy_blocks_ref", "quantize_pool_ref", "E4M3_MAX", "bf16_to_f32",
     "bf16_to_f64", "e4m3_encode", "e4m3_quantize", "e4m3_table", "e4m3_to_f64", "e4m3_value",
     "attend", "decode_partitioned_ref", "decode_ref", "gather_kv", "lse_merge_ref", "multi_query_ref",
     "partition_stats", "to_f64", "decode_algorithmic_bytes", "internal_waste_tokens", "kv_bytes",
-    "pages_for",
+    "pages_for", "physical_kv_bytes",
 ]

@@ -43,3 +43,30 @@ def decode_algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, 
     if fp8_scales:
         total += pages * num_kv_heads * 2 * 4
     return total
+
+
+def physical_kv_bytes(block_tables, context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      kv_elem_bytes: int, q_rows: int, q_elem_bytes: int = 2, out_elem_bytes: int = 2,
+                      fp8_scales: bool = False) -> int:
+    """Bytes an attention step must move when every physical block is read
+    once, however many sequences reference it ("17 · 连续批处理与
+    PagedAttention", section 三: a shared block is stored once): for each
+    distinct physical block, its K and V rows up to the furthest token any
+    of its sequences uses; plus q and out rows (q_rows of them), the used
+    block-table entries, context lengths and (fp8) the used scales."""
+    visible = {}
+    pages = 0
+    for b, ctx in enumerate(context_lens):
+        ctx = int(ctx)
+        n = pages_for(ctx)
+        pages += n
+        for i in range(n):
+            blk = int(block_tables[b][i])
+            visible[blk] = max(visible.get(blk, 0), min(BLOCK, ctx - i * BLOCK))
+    tokens = sum(visible.values())
+    total = tokens * num_kv_heads * head_dim * 2 * kv_elem_bytes
+    total += q_rows * num_q_heads * head_dim * (q_elem_bytes + out_elem_bytes)
+    total += pages * 4 + 4 * len(context_lens)
+    if fp8_scales:
+        total += len(visible) * num_kv_heads * 2 * 4
+    return total

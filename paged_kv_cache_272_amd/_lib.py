@@ -46,7 +46,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("num_q_tokens", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
                 ("head_dim", _i32), ("num_items", _i32), ("num_columns", _i32), ("num_records", _i32),
                 ("num_merge_rows", _i32), ("num_merge_entries", _i32), ("num_shared_groups", _i32),
-                ("reserved", _i32), ("plan_bytes", _i64), ("workspace_bytes", _i64), ("block_reads", _i64)]
+                ("num_wgs", _i32), ("max_item_columns", _i32), ("reserved", _i32), ("plan_bytes", _i64),
+                ("workspace_bytes", _i64), ("block_reads", _i64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -230,7 +231,7 @@ def _host_i32(a, name: str) -> Optional[np.ndarray]:
 
 def pa_plan_attention(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, q_start=None,
                       block_tables=None, share_prefix: bool = False,
-                      target_items: int = 0) -> Tuple[np.ndarray, PlanInfo]:
+                      target_slices: int = 0) -> Tuple[np.ndarray, PlanInfo]:
     """Build a plan on the host (host int32 arrays).  Returns (plan bytes, info).
 
     q_start [B+1] (None: one new token per sequence); block_tables [B, MB]
@@ -248,7 +249,7 @@ def pa_plan_attention(context_lens, num_q_heads: int, num_kv_heads: int, head_di
         raise ValueError("share_prefix needs the host block tables")
     info = PlanInfo()
     args = [None if qs is None else qs.ctypes.data, cl.ctypes.data, None if bt is None else bt.ctypes.data, mb, b,
-            num_q_heads, num_kv_heads, head_dim, flags, int(target_items)]
+            num_q_heads, num_kv_heads, head_dim, flags, int(target_slices)]
     _check(_lib.pa_plan_attention(*args, None, 0, ctypes.byref(info)), "pa_plan_attention")
     plan = np.zeros(max(16, info.plan_bytes), dtype=np.uint8)
     _check(_lib.pa_plan_attention(*args, plan.ctypes.data, plan.nbytes, ctypes.byref(info)), "pa_plan_attention")

@@ -7,9 +7,10 @@
 // (the causal mask of section 3.3, aligned to the end of the context), with
 // K/V gathered page by page through the block table (section 2.3).
 //
-// One workgroup per plan item, one wave per KV head.  A wave loads each
-// 16-token K/V block of the item's run once and applies it to the item's
-// (up to 16) query columns as the N dimension of the MFMAs (mfma_tile.h);
+// One workgroup per slice of the plan (a list of items), one wave per KV
+// head.  A wave loads each 16-token K/V block of an item's run once and
+// applies it to the item's query columns (up to two tiles of 16) as the N
+// dimension of the MFMAs (mfma_tile.h);
 // columns may belong to different tokens of one sequence or to different
 // sequences that share the block.  An item that is its columns' only
 // contribution writes the output; otherwise it leaves (m, l, acc) partials
@@ -33,25 +34,32 @@ struct PlannedPending {
   float ks, vs;
 };
 
-template <int D, bool kFp8>
-__global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(PlannedArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// One plan item on one wave (KV head g): stream the item's blocks through
+// kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
+// write the output or the partial records.
+template <int D, bool kFp8, int kTiles>
+__device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, int g, int lane) {
   const int r = lane & 15, c = lane >> 4;
-  const int g = blockIdx.y * a.waves_per_wg + wave;
-  if (g >= a.num_kv_heads) return;
-  const PlanItem it = a.items[blockIdx.x];
-  const int ncols = min(it.ncols, 16);
+  const int ncols = min(it.ncols, 16 * kTiles);
   if (ncols <= 0) return;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int seq = clampi(it.seq, 0, a.num_seqs - 1);
 
-  // this lane's query column (lanes r >= ncols carry a zero column that sees nothing)
-  PlanColumn col{0, 0, 0, 0};
-  if (r < ncols) col = a.cols[clampi(it.col0 + r, 0, a.num_columns - 1)];
-  const int64_t row = (int64_t)clampi(col.q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
-                      clampi(col.j, 0, G - 1);
-  HeadState<D, kFp8> hs;
-  hs.begin_row(reinterpret_cast<const uint16_t*>(a.q), r < ncols ? row : -1, c);
+  // this lane's query column in each tile (columns past ncols are zero and see nothing)
+  int horizon[kTiles];
+  int64_t row[kTiles];
+  HeadState<D, kFp8> hs[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    PlanColumn col{0, 0, 0, 0};
+    const bool live = 16 * t + r < ncols;
+    if (live) col = a.cols[clampi(it.col0 + 16 * t + r, 0, a.num_columns - 1)];
+    horizon[t] = col.horizon;
+    row[t] = (int64_t)clampi(col.q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
+             clampi(col.j, 0, G - 1);
+    hs[t].begin_row(reinterpret_cast<const uint16_t*>(a.q), live ? row[t] : -1, c);
+  }
+  const bool second = kTiles > 1 && ncols > 16;     // wave-uniform
 
   const int lo = max(it.blk_lo, 0), hi = min(it.blk_hi, a.max_blocks_per_seq);
   const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
@@ -84,7 +92,9 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
   auto consume = [&](const PlannedPending<D, kFp8>& p) {
     const int t0 = p.i * kBlockTokens;
     const int valid = min(kBlockTokens, it.kv_len - t0);
-    hs.step_cols(p.regs, valid, col.horizon - t0, a.scale_log2 * p.ks, p.vs, c);
+    hs[0].step_cols(p.regs, valid, horizon[0] - t0, a.scale_log2 * p.ks, p.vs, c);
+    if constexpr (kTiles > 1)
+      if (second) hs[1].step_cols(p.regs, valid, horizon[1] - t0, a.scale_log2 * p.ks, p.vs, c);
   };
 
   // software pipeline: the next block's loads are in flight while this one computes
@@ -99,21 +109,36 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
     }
   }
 
-  const float L = hs.total_l();
-  float o[4 * Tile<D, kFp8>::kE];
-  hs.unpack(o);
-  if (r >= ncols) return;
   const int d0 = (D / 4) * c;
-  if (it.rec0 < 0) {
-    store_bf16_run<D>(reinterpret_cast<uint16_t*>(a.out) + row * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
-  } else {
-    const int64_t wr = (int64_t)clampi(it.rec0 + r, 0, a.num_records - 1) * a.num_kv_heads + g;
-    store_f32_run<D>(a.ws_acc + wr * D, d0, o);
-    if (c == 0) {
-      a.ws_m[wr] = hs.m;
-      a.ws_l[wr] = L;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    if (t > 0 && !second) break;
+    const float L = hs[t].total_l();
+    float o[4 * Tile<D, kFp8>::kE];
+    hs[t].unpack(o);
+    if (16 * t + r >= ncols) continue;
+    if (it.rec0 < 0) {
+      store_bf16_run<D>(reinterpret_cast<uint16_t*>(a.out) + row[t] * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
+    } else {
+      const int64_t wr = (int64_t)clampi(it.rec0 + 16 * t + r, 0, a.num_records - 1) * a.num_kv_heads + g;
+      store_f32_run<D>(a.ws_acc + wr * D, d0, o);
+      if (c == 0) {
+        a.ws_m[wr] = hs[t].m;
+        a.ws_l[wr] = L;
+      }
     }
   }
+}
+
+// Workgroup x runs the items of slice x in order, one wave per KV head.
+template <int D, bool kFp8, int kTiles>
+__global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(PlannedArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.y * a.waves_per_wg + wave;
+  if (g >= a.num_kv_heads) return;
+  const int k0 = clampi(a.wg_start[blockIdx.x], 0, a.num_items);
+  const int k1 = clampi(a.wg_start[blockIdx.x + 1], k0, a.num_items);
+  for (int k = k0; k < k1; ++k) run_item<D, kFp8, kTiles>(a, a.items[k], g, lane);
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's
@@ -173,16 +198,20 @@ __global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(Pla
 }  // namespace
 
 hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_items, a.head_groups);
+  const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
   const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
+  const bool two = a.max_item_columns > 16;
+#define PA_LAUNCH_PLANNED(D_, F_, T_) \
+  hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, 0, stream, a)
   if (a.head_dim == 128) {
-    if (fp8) hipLaunchKernelGGL((attend_planned_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attend_planned_kernel<128, false>), grid, block, 0, stream, a);
+    if (fp8) { if (two) PA_LAUNCH_PLANNED(128, true, 2); else PA_LAUNCH_PLANNED(128, true, 1); }
+    else { if (two) PA_LAUNCH_PLANNED(128, false, 2); else PA_LAUNCH_PLANNED(128, false, 1); }
   } else {
-    if (fp8) hipLaunchKernelGGL((attend_planned_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attend_planned_kernel<64, false>), grid, block, 0, stream, a);
+    if (fp8) { if (two) PA_LAUNCH_PLANNED(64, true, 2); else PA_LAUNCH_PLANNED(64, true, 1); }
+    else { if (two) PA_LAUNCH_PLANNED(64, false, 2); else PA_LAUNCH_PLANNED(64, false, 1); }
   }
+#undef PA_LAUNCH_PLANNED
   return hipGetLastError();
 }
 

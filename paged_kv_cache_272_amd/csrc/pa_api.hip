@@ -333,7 +333,8 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   if (!info) return PA_ERR_NULL_POINTER;
   const pa_plan_info& in = *info;
   if (in.num_seqs < 0 || in.num_q_tokens < 0 || in.num_items < 0 || in.num_columns < 0 || in.num_records < 0 ||
-      in.num_merge_rows < 0 || in.num_merge_entries < 0)
+      in.num_merge_rows < 0 || in.num_merge_entries < 0 || in.num_wgs < 0 || in.max_item_columns < 0 ||
+      in.max_item_columns > 32)
     return PA_ERR_BAD_SHAPE;
   if (in.num_q_heads < 1 || in.num_kv_heads < 1 || in.num_q_heads % in.num_kv_heads) return PA_ERR_BAD_SHAPE;
   if (in.num_q_heads / in.num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
@@ -345,7 +346,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   if ((int64_t)lay.bytes != in.plan_bytes) return PA_ERR_BAD_SHAPE;
   if ((int64_t)planned_workspace_bytes(in) != in.workspace_bytes) return PA_ERR_BAD_SHAPE;
   if (in.num_items == 0 || in.num_seqs == 0 || in.num_q_tokens == 0) return PA_OK;
-  if (in.num_columns < 1) return PA_ERR_BAD_SHAPE;
+  if (in.num_columns < 1 || in.num_wgs < 1) return PA_ERR_BAD_SHAPE;
   if (in.num_merge_rows > 0 && (in.num_records < 1 || in.num_merge_entries < 1)) return PA_ERR_BAD_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !plan) return PA_ERR_NULL_POINTER;
   if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
@@ -368,6 +369,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   a.cols = reinterpret_cast<const PlanColumn*>(p + lay.cols_off);
   a.rows = reinterpret_cast<const PlanMergeRow*>(p + lay.rows_off);
   a.entries = reinterpret_cast<const int32_t*>(p + lay.entries_off);
+  a.wg_start = reinterpret_cast<const int32_t*>(p + lay.wg_off);
   if (ws_need > 0) {
     const size_t rows = (size_t)in.num_records * in.num_kv_heads;
     float* ws = static_cast<float*>(workspace);
@@ -380,6 +382,8 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   a.num_records = in.num_records;
   a.num_merge_rows = in.num_merge_rows;
   a.num_merge_entries = in.num_merge_entries;
+  a.num_wgs = in.num_wgs;
+  a.max_item_columns = in.max_item_columns;
   a.num_seqs = in.num_seqs;
   a.num_q_tokens = in.num_q_tokens;
   a.num_q_heads = in.num_q_heads;

@@ -111,15 +111,16 @@ size_t align_floats(size_t n);
 
 // ---- planned attention (pa_plan_attention / pa_attend_planned)
 //
-// A packed plan is four arrays, one after the other (each 16-byte aligned):
+// A packed plan is five arrays, one after the other (each 16-byte aligned):
 //   items[num_items], columns[num_columns], merge_rows[num_merge_rows],
-//   entries[num_merge_entries] (int32 record ids).
+//   entries[num_merge_entries] (int32 record ids), wg_start[num_wgs + 1]
+//   (workgroup x runs items wg_start[x] .. wg_start[x+1]-1).
 // Item k reads logical blocks [blk_lo, blk_hi) of block-table row `seq` for
 // the `ncols` query columns columns[col0 .. col0+ncols-1]; tokens at or past
 // kv_len hold no data.  rec0 < 0: the item is the column's only
 // contribution and writes `out`; otherwise column c's partial result goes
 // to record rec0 + c.  A merge row combines the records entries[e0 .. e0+n-1]
-// into the output row of (q_row, j).  ncols == 0 marks an empty item.
+// into the output row of (q_row, j).
 struct PlanItem {
   int32_t seq, blk_lo, blk_hi, col0, ncols, kv_len, rec0, pad;
 };
@@ -131,7 +132,7 @@ struct PlanMergeRow {
 };
 
 struct PlanLayout {
-  size_t items_off, cols_off, rows_off, entries_off, bytes;
+  size_t items_off, cols_off, rows_off, entries_off, wg_off, bytes;
 };
 
 inline size_t align16(size_t n) { return (n + 15) / 16 * 16; }
@@ -142,7 +143,8 @@ inline PlanLayout plan_layout(const pa_plan_info& info) {
   l.cols_off = align16(l.items_off + (size_t)info.num_items * sizeof(PlanItem));
   l.rows_off = align16(l.cols_off + (size_t)info.num_columns * sizeof(PlanColumn));
   l.entries_off = align16(l.rows_off + (size_t)info.num_merge_rows * sizeof(PlanMergeRow));
-  l.bytes = align16(l.entries_off + (size_t)info.num_merge_entries * sizeof(int32_t));
+  l.wg_off = align16(l.entries_off + (size_t)info.num_merge_entries * sizeof(int32_t));
+  l.bytes = align16(l.wg_off + (size_t)(info.num_wgs > 0 ? info.num_wgs + 1 : 0) * sizeof(int32_t));
   return l;
 }
 
@@ -166,10 +168,11 @@ struct PlannedArgs {
   const PlanColumn* cols;
   const PlanMergeRow* rows;
   const int32_t* entries;
+  const int32_t* wg_start;
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int32_t num_items, num_columns, num_records, num_merge_rows, num_merge_entries;
+  int32_t num_items, num_columns, num_records, num_merge_rows, num_merge_entries, num_wgs, max_item_columns;
   int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, num_blocks;
   int32_t waves_per_wg, head_groups;

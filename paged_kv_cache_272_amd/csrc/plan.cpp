@@ -1,9 +1,9 @@
 // Host planner for pa_attend_planned: cuts attention over the paged cache
-// into work items of at most 16 query columns by a run of 16-token blocks.
+// into work items of at most 32 query columns by a run of 16-token blocks.
 //
 // A query column is one (new token, query head within its GQA group) pair;
-// it becomes one N-column of the MFMA tile, so up to 16 of them share every
-// K/V block a wave loads.  New token i of a sequence with q_len new tokens
+// it becomes one N-column of an MFMA tile.  A wave holds up to two tiles of
+// 16 columns, so up to 32 columns share every K/V block the wave loads.  New token i of a sequence with q_len new tokens
 // and context ctx sits at position ctx - q_len + i and sees positions
 // 0 .. ctx - q_len + i (the causal mask of "系统级优化…" section 3.3,
 // aligned to the end of the context; the multi-token steps are chunked
@@ -18,11 +18,12 @@
 // remaining blocks.  Partial results of a column's segments are merged by
 // log-sum-exp (exact in real arithmetic).
 //
-// Work balance: every tile's block run is cut into near-equal pieces of
-// about total_blocks / target_items blocks (at least kMinChunk).  Items that
-// read the same blocks (tiles of one segment) are kept on one XCD: the GPU
-// hands workgroup x to XCD x mod 8, so the planner fills 8 queues with
-// bundles of sibling items (least-loaded queue first) and interleaves them.
+// Work balance: the tiles' block runs are laid end to end (the tiles of one
+// segment taking turns piece by piece) and cut into about 2048 / (waves per
+// workgroup) equal slices, one workgroup each, as the balanced decode does
+// with sequences; every (run, slice) overlap is an item, and a workgroup
+// runs its slice's items in order.  No compute unit idles at the end of the
+// launch for lack of work.
 #include <algorithm>
 #include <cstring>
 #include <map>
@@ -34,9 +35,9 @@ namespace pa {
 namespace {
 
 constexpr int kBlockTokens = PA_BLOCK_SIZE;
-constexpr int kMinChunk = 16;          // blocks per item, at least
-constexpr int kDefaultTargetItems = 1024;
-constexpr int kXcds = 8;
+constexpr int kTileCols = 32;          // query columns per item (two 16-column MFMA tiles)
+constexpr int kTargetWaves = 2048;     // waves over the device, about 8 per compute unit
+constexpr int kMaxWavesPerWg = 8;      // one wave per KV head, at most 8 per workgroup
 
 struct Segment {
   int seq;                       // block-table row the blocks are read from
@@ -47,6 +48,7 @@ struct Segment {
 
 struct PlanBuild {
   std::vector<PlanItem> items;
+  std::vector<int32_t> wg_start;       // [num_wgs + 1]: workgroup x runs items wg_start[x] .. wg_start[x+1]-1
   std::vector<PlanColumn> cols;
   std::vector<PlanMergeRow> rows;
   std::vector<int32_t> entries;
@@ -65,7 +67,7 @@ void sequence_columns(int q0, int q_len, int G, std::vector<int>& out) {
 
 int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_t* block_tables,
                int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t flags, int32_t target_items, PlanBuild& pb) {
+               int32_t flags, int32_t target_slices, PlanBuild& pb) {
   const int G = num_q_heads / num_kv_heads;
   const bool share = (flags & PA_PLAN_SHARE_PREFIX) != 0;
   const int64_t B = num_seqs;
@@ -139,7 +141,7 @@ int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_
     segs.push_back(std::move(s));
   }
 
-  // ---- tiles (16 columns each) and their block runs
+  // ---- tiles (up to kTileCols columns each) and their block runs
   struct Tile {
     int seg, col0, ncols, lo, hi, kv_len;
   };
@@ -147,8 +149,8 @@ int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_
   int64_t total = 0;
   for (size_t si = 0; si < segs.size(); ++si) {
     const Segment& s = segs[si];
-    for (size_t c0 = 0; c0 < s.cols.size(); c0 += 16) {
-      const int n = (int)std::min<size_t>(16, s.cols.size() - c0);
+    for (size_t c0 = 0; c0 < s.cols.size(); c0 += kTileCols) {
+      const int n = (int)std::min<size_t>(kTileCols, s.cols.size() - c0);
       int max_h = 0;
       for (int k = 0; k < n; ++k) max_h = std::max(max_h, (int)pb.cols[s.cols[c0 + k]].horizon);
       const int hi = std::min(s.hi, ceil_div(max_h, kBlockTokens));
@@ -157,76 +159,91 @@ int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_
       total += hi - s.lo;
     }
   }
-  const int target = target_items > 0 ? target_items : kDefaultTargetItems;
-  const int chunk = std::max<int>(kMinChunk, ceil_div(total, target));
-
-  // ---- items, records and bundles of sibling items (same blocks, other tiles)
-  std::vector<std::vector<int>> col_recs(pb.cols.size());
-  std::vector<PlanColumn> item_cols;                 // columns laid out per item
-  std::vector<PlanItem> raw;
-  std::vector<std::pair<int, int>> bundles;          // [first, last) into raw
-  std::vector<int64_t> bundle_load;
-  // the tiles of one segment are consecutive; cut each into the same pieces
+  // ---- runs of units in work order.  A segment with one tile is one run; the
+  // tiles of a segment with several tiles (the same blocks, other columns)
+  // take turns piece by piece, so they read each piece at about the same
+  // time and the second read is served from cache.
+  const int waves_per_wg = std::min(num_kv_heads, kMaxWavesPerWg);
+  const int head_groups = ceil_div(num_kv_heads, waves_per_wg);
+  const int64_t want = target_slices > 0 ? target_slices : std::max(1, kTargetWaves / (waves_per_wg * head_groups));
+  const int n = (int)std::min<int64_t>(want, total);             // slices; none is empty
+  const int piece = std::max(1, ceil_div(total, std::max(n, 1)));
+  struct Run {
+    int tile, lo, hi;
+  };
+  std::vector<Run> runs;
   for (size_t t0 = 0; t0 < tiles.size();) {
     size_t t1 = t0;
     while (t1 < tiles.size() && tiles[t1].seg == tiles[t0].seg) ++t1;
-    const Segment& s = segs[tiles[t0].seg];
-    // pieces of the segment's longest run; a tile uses the pieces that overlap its run
-    int seg_hi = s.lo;
-    for (size_t t = t0; t < t1; ++t) seg_hi = std::max(seg_hi, tiles[t].hi);
-    const int len = seg_hi - s.lo;
-    const int pieces = std::max(1, ceil_div(len, chunk));
-    for (int p = 0; p < pieces; ++p) {
-      const int lo = s.lo + (int)((int64_t)p * len / pieces);
-      const int hi = s.lo + (int)((int64_t)(p + 1) * len / pieces);
-      const int first = (int)raw.size();
-      int64_t load = 0;
-      for (size_t t = t0; t < t1; ++t) {
-        const Tile& tl = tiles[t];
-        const int ilo = lo, ihi = std::min(hi, tl.hi);
-        if (ihi <= ilo) continue;
-        const bool direct = !s.partial && pieces == 1;
-        PlanItem it{};
-        it.seq = s.seq;
-        it.blk_lo = ilo;
-        it.blk_hi = ihi;
-        it.col0 = (int32_t)item_cols.size();
-        it.ncols = tl.ncols;
-        it.kv_len = tl.kv_len;
-        it.rec0 = direct ? -1 : pb.records;
-        for (int k = 0; k < tl.ncols; ++k) {
-          const int id = s.cols[tl.col0 + k];
-          item_cols.push_back(pb.cols[id]);
-          if (!direct) col_recs[id].push_back(pb.records + k);
+    if (t1 - t0 == 1) {
+      runs.push_back(Run{(int)t0, tiles[t0].lo, tiles[t0].hi});
+    } else {
+      int seg_hi = tiles[t0].lo;
+      for (size_t t = t0; t < t1; ++t) seg_hi = std::max(seg_hi, tiles[t].hi);
+      for (int lo = tiles[t0].lo; lo < seg_hi; lo += piece)
+        for (size_t t = t0; t < t1; ++t) {
+          const int hi = std::min(lo + piece, tiles[t].hi);
+          if (hi > lo) runs.push_back(Run{(int)t, lo, hi});
         }
-        if (!direct) pb.records += tl.ncols;
-        raw.push_back(it);
-        load += ihi - ilo;
-        pb.block_reads += ihi - ilo;
-      }
-      if ((int)raw.size() > first) {
-        bundles.emplace_back(first, (int)raw.size());
-        bundle_load.push_back(load);
-      }
     }
     t0 = t1;
   }
 
-  // ---- XCD queues: a bundle's items go to one queue, in order
-  std::vector<std::vector<int>> queue(kXcds);
-  std::vector<int64_t> qload(kXcds, 0);
-  for (size_t k = 0; k < bundles.size(); ++k) {
-    const int q = (int)(std::min_element(qload.begin(), qload.end()) - qload.begin());
-    for (int i = bundles[k].first; i < bundles[k].second; ++i) queue[q].push_back(i);
-    qload[q] += bundle_load[k];
+  // ---- cut the runs at slice boundaries: slice x owns units
+  // [floor(x*total/n), floor((x+1)*total/n)); every (run, slice) overlap is an item
+  struct Cut {
+    int tile, lo, hi, slice;
+  };
+  std::vector<Cut> cuts;
+  std::vector<int> items_of_tile(tiles.size(), 0);
+  {
+    int64_t u = 0;
+    int x = 0;
+    for (const Run& r : runs) {
+      int lo = r.lo;
+      while (lo < r.hi) {
+        while (x + 1 < n && (int64_t)(x + 1) * total / n <= u) ++x;
+        const int64_t slice_end = (int64_t)(x + 1) * total / n;
+        const int take = (int)std::min<int64_t>(r.hi - lo, slice_end - u);
+        cuts.push_back(Cut{r.tile, lo, lo + take, x});
+        ++items_of_tile[r.tile];
+        lo += take;
+        u += take;
+      }
+    }
   }
-  size_t depth = 0;
-  for (auto& q : queue) depth = std::max(depth, q.size());
+
+  // ---- items, records and the slices' item ranges
+  std::vector<std::vector<int>> col_recs(pb.cols.size());
+  std::vector<PlanColumn> item_cols;                 // columns laid out per item
+  std::vector<int32_t> tile_col0(tiles.size(), -1);  // a tile's columns are laid out once
   pb.items.clear();
-  pb.items.reserve(depth * kXcds);
-  const PlanItem empty{0, 0, 0, 0, 0, 0, -1, 0};
-  for (size_t d = 0; d < depth; ++d)
-    for (int q = 0; q < kXcds; ++q) pb.items.push_back(d < queue[q].size() ? raw[queue[q][d]] : empty);
+  pb.wg_start.assign(n > 0 ? (size_t)n + 1 : 0, 0);
+  for (const Cut& ct : cuts) {
+    const Tile& tl = tiles[ct.tile];
+    const Segment& s = segs[tl.seg];
+    const bool direct = !s.partial && items_of_tile[ct.tile] == 1;
+    if (tile_col0[ct.tile] < 0) {
+      tile_col0[ct.tile] = (int32_t)item_cols.size();
+      for (int k = 0; k < tl.ncols; ++k) item_cols.push_back(pb.cols[s.cols[tl.col0 + k]]);
+    }
+    PlanItem it{};
+    it.seq = s.seq;
+    it.blk_lo = ct.lo;
+    it.blk_hi = ct.hi;
+    it.col0 = tile_col0[ct.tile];
+    it.ncols = tl.ncols;
+    it.kv_len = tl.kv_len;
+    it.rec0 = direct ? -1 : pb.records;
+    if (!direct) {
+      for (int k = 0; k < tl.ncols; ++k) col_recs[s.cols[tl.col0 + k]].push_back(pb.records + k);
+      pb.records += tl.ncols;
+    }
+    pb.items.push_back(it);
+    pb.block_reads += ct.hi - ct.lo;
+    pb.wg_start[ct.slice + 1] = (int32_t)pb.items.size();
+  }
+  for (int x = 1; x <= n; ++x) pb.wg_start[x] = std::max(pb.wg_start[x], pb.wg_start[x - 1]);
   pb.cols = std::move(item_cols);
 
   // ---- merge rows: every column with partial records, in column order
@@ -246,7 +263,7 @@ using namespace pa;
 
 PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_lens, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
-                                int32_t num_kv_heads, int32_t head_dim, int32_t flags, int32_t target_items,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t flags, int32_t target_slices,
                                 void* plan, size_t plan_capacity, pa_plan_info* info) {
   if (!info) return PA_ERR_NULL_POINTER;
   std::memset(info, 0, sizeof(*info));
@@ -254,12 +271,12 @@ PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_l
   if (num_q_heads % num_kv_heads) return PA_ERR_BAD_SHAPE;
   if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (target_items < 0 || (flags & ~PA_PLAN_SHARE_PREFIX)) return PA_ERR_BAD_SHAPE;
+  if (target_slices < 0 || (flags & ~PA_PLAN_SHARE_PREFIX)) return PA_ERR_BAD_SHAPE;
   if (num_seqs > 0 && !context_lens) return PA_ERR_NULL_POINTER;
   if ((flags & PA_PLAN_SHARE_PREFIX) && num_seqs > 0 && !block_tables) return PA_ERR_NULL_POINTER;
   PlanBuild pb;
   const int st = build_plan(q_start, context_lens, block_tables, max_blocks_per_seq, num_seqs, num_q_heads,
-                            num_kv_heads, flags, target_items, pb);
+                            num_kv_heads, flags, target_slices, pb);
   if (st != PA_OK) return st;
   info->num_seqs = num_seqs;
   info->num_q_tokens = q_start ? q_start[num_seqs] : num_seqs;
@@ -272,6 +289,8 @@ PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_l
   info->num_merge_rows = (int32_t)pb.rows.size();
   info->num_merge_entries = (int32_t)pb.entries.size();
   info->num_shared_groups = pb.groups;
+  info->num_wgs = pb.wg_start.empty() ? 0 : (int32_t)pb.wg_start.size() - 1;
+  for (const PlanItem& it : pb.items) info->max_item_columns = std::max(info->max_item_columns, it.ncols);
   const PlanLayout lay = plan_layout(*info);
   info->plan_bytes = (int64_t)lay.bytes;
   info->workspace_bytes = (int64_t)planned_workspace_bytes(*info);
@@ -285,5 +304,7 @@ PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_l
   if (!pb.rows.empty()) std::memcpy(p + lay.rows_off, pb.rows.data(), pb.rows.size() * sizeof(PlanMergeRow));
   if (!pb.entries.empty())
     std::memcpy(p + lay.entries_off, pb.entries.data(), pb.entries.size() * sizeof(int32_t));
+  if (!pb.wg_start.empty())
+    std::memcpy(p + lay.wg_off, pb.wg_start.data(), pb.wg_start.size() * sizeof(int32_t));
   return PA_OK;
 }

@@ -20,6 +20,7 @@ def unpack_plan(plan: np.ndarray, info) -> dict:
     cols_off = _align16(items_off + info.num_items * 32)
     rows_off = _align16(cols_off + info.num_columns * 16)
     ent_off = _align16(rows_off + info.num_merge_rows * 16)
+    wg_off = _align16(ent_off + info.num_merge_entries * 4)
     raw = plan.view(np.uint8)
 
     def view(off, n, width):
@@ -32,6 +33,7 @@ def unpack_plan(plan: np.ndarray, info) -> dict:
         "cols": view(cols_off, info.num_columns, 4),
         "rows": view(rows_off, info.num_merge_rows, 4),
         "entries": raw[ent_off:ent_off + info.num_merge_entries * 4].view(np.int32),
+        "wg_start": raw[wg_off:wg_off + (info.num_wgs + 1 if info.num_wgs else 0) * 4].view(np.int32),
     }
 
 
@@ -50,7 +52,7 @@ def check_coverage(plan: np.ndarray, info, q_start, context_lens, block_tables, 
         if it["ncols"][k] == 0:
             continue
         seq, lo, hi, c0, nc, rec0 = (int(it[n][k]) for n in ("seq", "blk_lo", "blk_hi", "col0", "ncols", "rec0"))
-        assert 1 <= nc <= 16 and lo < hi
+        assert 1 <= nc <= 32 and lo < hi
         for c in range(nc):
             q_row, j, horizon, _ = (int(x) for x in p["cols"][c0 + c])
             key = (q_row, j)

@@ -18,7 +18,7 @@ def _run(dw, wl, share=False, target=0, workspace=None, tables=None):
     tables_host, tables_dev = (wl.block_tables, dw.block_tables) if tables is None else tables
     plan, info = pa.pa_plan_attention(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                       q_start=wl.q_start, block_tables=tables_host if share else None,
-                                      share_prefix=share, target_items=target)
+                                      share_prefix=share, target_slices=target)
     out = torch.empty_like(dw.q)
     pa.pa_attend_planned(out, dw.q, dw.k_cache, dw.v_cache, tables_dev, wl.scale, pa.plan_to_device(plan),
                          info, dw.k_scale, dw.v_scale, workspace=workspace)
@@ -45,7 +45,7 @@ def test_multi_query_parity(hq, hkv, d, kv):
     q_lens = [5, 7, 0, 16, 1, 37, 1, 4]
     wl, dw, want = _multi_query_case("mq", 201, ctxs, q_lens, hq, hkv, d, kv)
     for target in (0, 5, 3000):
-        log(f"multi-query hq={hq} hkv={hkv} d={d} kv={kv} target_items={target}")
+        log(f"multi-query hq={hq} hkv={hkv} d={d} kv={kv} target_slices={target}")
         out, info = _run(dw, wl, target=target)
         err = float(np.abs(out_to_f64(out) - want).max())
         log(f"  items={info.num_items} records={info.num_records} max abs error {err:.3e}")
@@ -137,7 +137,7 @@ def test_shared_prefix_decode_parity(kv):
 
 def test_planned_stale_workspace():
     wl, dw, want = _multi_query_case("mq-stale", 206, [300, 40], [20, 40], 32, 8, 128, "bf16")
-    plan, info = pa.pa_plan_attention(wl.context_lens, 32, 8, 128, q_start=wl.q_start, target_items=9)
+    plan, info = pa.pa_plan_attention(wl.context_lens, 32, 8, 128, q_start=wl.q_start, target_slices=9)
     assert info.workspace_bytes > 0
     ws = torch.full((info.workspace_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dw.q)

@@ -37,10 +37,12 @@ def test_decode_plan_covers_every_column(target):
     rng = np.random.default_rng(3)
     ctxs = [1, 15, 16, 17, 300, 513, 4096, 2, 1000]
     bt = _tables(ctxs, rng)
-    plan, info = pa.pa_plan_attention(np.array(ctxs), 32, 8, 128, target_items=target)
+    plan, info = pa.pa_plan_attention(np.array(ctxs), 32, 8, 128, target_slices=target)
     check_coverage(plan, info, np.arange(len(ctxs) + 1), ctxs, bt, 4)
-    assert info.num_items % 8 == 0
+    check_slices(plan, info)
     assert info.num_shared_groups == 0
+    if target:
+        assert info.num_wgs == min(target, info.block_reads)
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (8, 8), (16, 1)])
@@ -51,7 +53,7 @@ def test_multi_query_plan_covers_causal_runs(hq, hkv):
     bt = _tables(ctxs, rng)
     for target in (0, 3, 40):
         plan, info = pa.pa_plan_attention(np.array(ctxs), hq, hkv, 128, q_start=_q_start(q_lens),
-                                          target_items=target)
+                                          target_slices=target)
         check_coverage(plan, info, _q_start(q_lens), ctxs, bt, hq // hkv)
         assert info.num_q_tokens == sum(q_lens)
 
@@ -72,22 +74,55 @@ def test_shared_prefix_plan_reads_prefix_once():
     assert info.block_reads == per_seq - 3 * 3 * (4 - 1)
 
 
-def test_xcd_order_keeps_siblings_together():
-    """Tiles of one segment that read the same blocks sit at item indices equal mod 8."""
-    wl = W.make_shared_prefix_workload(name="share8", seed=6, num_prompts=4, samples_per_prompt=8,
+def check_slices(plan, info):
+    """Workgroup x runs items wg_start[x] .. wg_start[x+1]-1; every item belongs
+    to exactly one workgroup and the workgroups' block counts differ by at most one."""
+    p = unpack_plan(plan, info)
+    ws, it = p["wg_start"], p["items"]
+    if info.num_items == 0:
+        assert info.num_wgs == 0
+        return
+    assert ws[0] == 0 and ws[-1] == info.num_items and np.all(np.diff(ws) >= 1)
+    loads = [int((it["blk_hi"][ws[x]:ws[x + 1]] - it["blk_lo"][ws[x]:ws[x + 1]]).sum()) for x in range(info.num_wgs)]
+    assert max(loads) - min(loads) <= 1 and sum(loads) == info.block_reads
+
+
+def test_default_slices_fill_the_device():
+    """About 2048 waves: 256 workgroups of 8 waves for 8 KV heads, 2048 of one wave for one."""
+    ctxs = np.full(64, 4096)
+    for hkv, want in ((8, 256), (1, 2048), (16, 128), (4, 512)):
+        plan, info = pa.pa_plan_attention(ctxs, hkv * 4 if hkv < 16 else 16, hkv, 128)
+        assert info.num_wgs == want, (hkv, info.num_wgs)
+        check_slices(plan, info)
+    plan, info = pa.pa_plan_attention(np.array([5, 20]), 32, 8, 128)   # 3 blocks: 3 slices
+    assert info.num_wgs == 3
+
+
+def test_sibling_tiles_take_turns():
+    """16 samples x 4 heads = 64 columns: two items of 32 columns read each piece
+    of the shared prefix one after the other (adjacent items); 8 samples x 4
+    heads fit one item, so each prefix block is read once."""
+    wl = W.make_shared_prefix_workload(name="share16", seed=6, num_prompts=4, samples_per_prompt=16,
                                        prefix_tokens=160, suffix_max=64, num_q_heads=32, num_kv_heads=8,
                                        head_dim=128, with_values=False)
     plan, info = pa.pa_plan_attention(wl.context_lens, 32, 8, 128, block_tables=wl.block_tables,
-                                      share_prefix=True, target_items=64)
+                                      share_prefix=True, target_slices=64)
+    check_coverage(plan, info, np.arange(wl.num_seqs + 1), wl.context_lens, wl.block_tables, 4)
+    check_slices(plan, info)
     it = unpack_plan(plan, info)["items"]
-    where = {}
-    for k in range(info.num_items):
-        if it["ncols"][k]:
-            where.setdefault((int(it["seq"][k]), int(it["blk_lo"][k]), int(it["blk_hi"][k])), []).append(k)
-    shared = [v for v in where.values() if len(v) > 1]
-    assert shared, "8 samples x 4 heads = 32 columns should give sibling tiles"
-    for ks in shared:
-        assert len({k % 8 for k in ks}) == 1, ks
+    pairs = sum(1 for k in range(info.num_items - 1)
+                if (it["seq"][k], it["blk_lo"][k]) == (it["seq"][k + 1], it["blk_lo"][k + 1])
+                and it["col0"][k] != it["col0"][k + 1])
+    assert pairs >= 3, pairs       # a slice boundary may cut one of the 4 pairs
+    wl8 = W.make_shared_prefix_workload(name="share8", seed=6, num_prompts=4, samples_per_prompt=8,
+                                        prefix_tokens=160, suffix_max=64, num_q_heads=32, num_kv_heads=8,
+                                        head_dim=128, with_values=False)
+    plan, info = pa.pa_plan_attention(wl8.context_lens, 32, 8, 128, block_tables=wl8.block_tables_shared,
+                                      share_prefix=True)
+    shared_blocks = 4 * 10
+    per_seq = sum(-(-int(c) // 16) for c in wl8.context_lens)
+    assert info.max_item_columns == 32
+    assert info.block_reads == per_seq - shared_blocks * (8 - 1)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -102,7 +137,7 @@ def test_plan_executed_on_cpu_matches_oracle_multi_query(kv):
     want = oracle.multi_query_ref(wl.q, wl.q_start, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
                                   wl.k_scale, wl.v_scale)
     for target in (0, 2, 9):
-        plan, info = pa.pa_plan_attention(wl.context_lens, 8, 2, 64, q_start=wl.q_start, target_items=target)
+        plan, info = pa.pa_plan_attention(wl.context_lens, 8, 2, 64, q_start=wl.q_start, target_slices=target)
         got = run_plan_cpu(plan, info, wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
                            wl.k_scale, wl.v_scale)
         assert np.abs(got - want).max() < 1e-12
@@ -116,7 +151,7 @@ def test_shared_prefix_plan_executed_on_cpu_matches_oracle_decode():
     k, v, _, _ = oracle.copy_blocks_ref(k, v, wl.copy_pairs)
     want = oracle.decode_ref(wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16")
     plan, info = pa.pa_plan_attention(wl.context_lens, 8, 2, 64, block_tables=wl.block_tables, share_prefix=True,
-                                      target_items=5)
+                                      target_slices=5)
     assert info.num_shared_groups == 2
     got = run_plan_cpu(plan, info, wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16")
     assert np.abs(got - want).max() < 1e-12
