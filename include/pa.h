@@ -63,7 +63,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -4,  /* head_dim or group size outside the supported set */
   PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than pa_decode_workspace_size() */
   PA_ERR_MISALIGNED = -6,   /* a q/out/cache pointer is not 16-byte aligned */
-  PA_ERR_LAUNCH = -7        /* the HIP runtime rejected a kernel launch */
+  PA_ERR_LAUNCH = -7,       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_OUT_OF_BLOCKS = -8 /* the block pool cannot hold the request (nothing changed) */
 } pa_status;
 
 /*
@@ -298,6 +299,71 @@ int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype,
                       int32_t num_blocks, float scale, const void* plan,
                       const pa_plan_info* info, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Host block manager and the continuous-batching step (host memory only).
+ *
+ * A global pool of num_blocks physical blocks of 16 tokens, one block table
+ * per sequence, and reference counts ("系统级优化…" section 2.3: one manager
+ * hands out equal pages, a request's pages need not be contiguous, pages a
+ * finished request frees are reused at once; "17 · 连续批处理与
+ * PagedAttention" section 三: blocks are shared by reference count and a
+ * shared block is copied only when a sharer writes into it).  A sequence of
+ * n tokens holds ceil(n/16) blocks.  Free blocks are handed out from the
+ * front of a free list that starts as `free_order` (NULL: 0..num_blocks-1);
+ * a freed block goes back to the front (reused first); a freed sequence
+ * releases its blocks last to first, so they come back in table order.
+ *
+ * Sequences are named by caller-chosen int32 ids.  Every call validates
+ * before it changes anything: a call that returns an error leaves the
+ * manager as it was.  OUT_OF_BLOCKS means the pool is too small for the
+ * request; the caller preempts (frees) a sequence and retries ("17 ·
+ * 连续批处理与 PagedAttention" section 五: running requests are evicted when
+ * the KV cache runs out, and recomputed later).  A manager is not
+ * thread-safe; distinct managers are independent.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+typedef struct pa_bm_stats {
+  int32_t num_blocks, free_blocks, num_seqs, reserved;
+  int64_t logical_tokens;   /* sum of the sequences' token counts */
+  int64_t block_refs;       /* sum of the sequences' block counts (shared blocks counted per sharer) */
+  int64_t stored_tokens;    /* tokens held in distinct blocks (a shared block counts once) */
+} pa_bm_stats;
+
+/* NULL if num_blocks < 1, free_order is not a permutation, or no memory. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, const int32_t* free_order);
+void pa_bm_destroy(pa_block_manager* m);
+/* A new sequence holding num_tokens tokens (a prompt): ceil(n/16) fresh blocks. */
+int pa_bm_add(pa_block_manager* m, int32_t seq, int32_t num_tokens);
+/* child references every block of parent (parallel sampling, beam search). */
+int pa_bm_fork(pa_block_manager* m, int32_t parent, int32_t child);
+/* Drop the sequence; blocks whose count reaches zero return to the pool. */
+int pa_bm_free(pa_block_manager* m, int32_t seq);
+/* One more token: returns its slot (block * 16 + offset); a new block when
+ * the last is full; when the last block is shared, a private copy
+ * (*cow_src -> *cow_dst, else both -1) whose contents the caller copies
+ * with pa_copy_blocks before writing the token. */
+int pa_bm_append(pa_block_manager* m, int32_t seq, int64_t* slot, int32_t* cow_src, int32_t* cow_dst);
+/* The sequence's block ids (table may be NULL to query the counts). */
+int pa_bm_table(const pa_block_manager* m, int32_t seq, int32_t* table, int32_t capacity,
+                int32_t* num_blocks, int64_t* num_tokens);
+int pa_bm_get_stats(const pa_block_manager* m, pa_bm_stats* out);
+/*
+ * One decode iteration of continuous batching ("17 · 连续批处理与
+ * PagedAttention" section 二: the batch is re-formed at every token): append
+ * one token to each of seqs[0..num_seqs-1] (distinct ids) and write the
+ * batch's arrays for pa_copy_blocks / pa_decode_append (or pa_cache_write +
+ * pa_decode): block_tables [num_seqs, max_blocks_per_seq] (unused entries
+ * repeat the last block), context_lens [num_seqs] (including the new
+ * token), slot_mapping [num_seqs] (the new token's slot), cow_pairs
+ * [num_seqs, 2] with *num_cow pairs used.  All or nothing: if the pool
+ * cannot hold the step, returns OUT_OF_BLOCKS with *blocks_short = how many
+ * blocks are missing, and changes nothing.
+ */
+int pa_bm_step(pa_block_manager* m, const int32_t* seqs, int32_t num_seqs, int32_t max_blocks_per_seq,
+               int32_t* block_tables, int32_t* context_lens, int64_t* slot_mapping, int32_t* cow_pairs,
+               int32_t* num_cow, int32_t* blocks_short);
 
 /* pa_status_string — static text for a status code (never NULL). */
 const char* pa_status_string(int status);

@@ -5,6 +5,7 @@ CPU-baseline leg of ``bench.py`` may import, call or execute anything in
 this package.  It shares no code with the GPU library and imports nothing
 from it; the two meet only through the seeded inputs of ``pa_workloads``.
 """
+from .block_manager_ref import BlockManagerRef, pages_for_tokens
 from .cache_ops import cache_write_ref, copy_blocks_ref, quantize_pool_ref
 from .formats import (E4M3_MAX, bf16_to_f32, bf16_to_f64, e4m3_encode, e4m3_quantize, e4m3_table,
                       e4m3_to_f64, e4m3_value)
@@ -13,6 +14,7 @@ from .paged_attention import (attend, decode_partitioned_ref, decode_ref, gather
 from .sizes import decode_algorithmic_bytes, internal_waste_tokens, kv_bytes, pages_for, physical_kv_bytes
 
 __all__ = [
+    "BlockManagerRef", "pages_for_tokens",
     "cache_write_ref", "copy_blocks_ref", "quantize_pool_ref", "E4M3_MAX", "bf16_to_f32",
     "bf16_to_f64", "e4m3_encode", "e4m3_quantize", "e4m3_table", "e4m3_to_f64", "e4m3_value",
     "attend", "decode_partitioned_ref", "decode_ref", "gather_kv", "lse_merge_ref", "multi_query_ref",

@@ -39,6 +39,13 @@ _lib = _load()
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 
 PA_PLAN_SHARE_PREFIX = 1
+PA_ERR_OUT_OF_BLOCKS = -8
+
+
+class BmStats(ctypes.Structure):
+    """pa_bm_stats (include/pa.h)."""
+    _fields_ = [("num_blocks", _i32), ("free_blocks", _i32), ("num_seqs", _i32), ("reserved", _i32),
+                ("logical_tokens", _i64), ("block_refs", _i64), ("stored_tokens", _i64)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -70,6 +77,16 @@ _SIGNATURES = {
                                          ctypes.POINTER(PlanInfo)]),
     "pa_attend_planned": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i32,
                                          _f32, _vp, ctypes.POINTER(PlanInfo), _vp, _sz, _vp]),
+    "pa_bm_create": (_vp, [_i32, _vp]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add": (ctypes.c_int, [_vp, _i32, _i32]),
+    "pa_bm_fork": (ctypes.c_int, [_vp, _i32, _i32]),
+    "pa_bm_free": (ctypes.c_int, [_vp, _i32]),
+    "pa_bm_append": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pa_bm_table": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
+    "pa_bm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(BmStats)]),
+    "pa_bm_step": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, ctypes.POINTER(_i32),
+                                  ctypes.POINTER(_i32)]),
     "pa_probe_sink_bytes": (_sz, []),
     "pa_probe_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "pa_probe_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -292,6 +309,87 @@ def prepare_attend_planned(out, q, k_cache, v_cache, block_tables, scale, plan, 
             ctypes.byref(info), _ptr(workspace), ws_bytes, _stream(stream))
     return PreparedCall("pa_attend_planned", args, (out, q, k_cache, v_cache, block_tables, k_scale, v_scale,
                                                     plan, info, workspace))
+
+
+class OutOfBlocks(PaError):
+    """The block pool cannot hold the request; ``blocks_short`` says by how much (steps only)."""
+
+    def __init__(self, where: str, blocks_short: int = 0):
+        super().__init__(PA_ERR_OUT_OF_BLOCKS, where)
+        self.blocks_short = blocks_short
+
+
+class HostBlockManager:
+    """The library's host block manager (pa_bm_*): a pool of 16-token blocks,
+    per-sequence tables, reference counts, copy-on-write and the
+    continuous-batching step.  Host memory only."""
+
+    def __init__(self, num_blocks: int, free_order=None):
+        order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        self._order = order
+        self._h = _lib.pa_bm_create(int(num_blocks), None if order is None else order.ctypes.data)
+        if not self._h:
+            raise PaError(-2, "pa_bm_create")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def _call(self, name, *args):
+        st = getattr(_lib, name)(self._h, *args)
+        if st == PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(name)
+        _check(st, name)
+
+    def add(self, seq: int, num_tokens: int) -> None:
+        self._call("pa_bm_add", int(seq), int(num_tokens))
+
+    def fork(self, parent: int, child: int) -> None:
+        self._call("pa_bm_fork", int(parent), int(child))
+
+    def free(self, seq: int) -> None:
+        self._call("pa_bm_free", int(seq))
+
+    def append(self, seq: int):
+        """(slot of the new token, (src, dst) copy pair or None)."""
+        slot, src, dst = _i64(), _i32(), _i32()
+        self._call("pa_bm_append", int(seq), ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def table(self, seq: int):
+        """(block ids as an int32 array, token count)."""
+        nb, nt = _i32(), _i64()
+        self._call("pa_bm_table", int(seq), None, 0, ctypes.byref(nb), ctypes.byref(nt))
+        out = np.zeros(max(nb.value, 1), dtype=np.int32)
+        self._call("pa_bm_table", int(seq), out.ctypes.data, out.size, ctypes.byref(nb), ctypes.byref(nt))
+        return out[:nb.value], nt.value
+
+    def stats(self) -> dict:
+        st = BmStats()
+        _check(_lib.pa_bm_get_stats(self._h, ctypes.byref(st)), "pa_bm_get_stats")
+        return {name: getattr(st, name) for name, _ in st._fields_ if name != "reserved"}
+
+    def step(self, seqs, max_blocks_per_seq: int, out=None):
+        """One decode iteration for ``seqs``: returns (block_tables [B, MB] int32,
+        context_lens [B] int32, slot_mapping [B] int64, copy pairs [n, 2] int32).
+        Raises OutOfBlocks (with ``blocks_short``) and changes nothing if the
+        pool cannot hold the step.  ``out`` may pass preallocated host arrays
+        (tables, lens, slots, pairs) to fill, e.g. pinned tensors' numpy views."""
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        b = ids.size
+        if out is None:
+            out = (np.zeros((b, max_blocks_per_seq), np.int32), np.zeros(b, np.int32), np.zeros(b, np.int64),
+                   np.zeros((max(b, 1), 2), np.int32))
+        bt, cl, sl, pr = out
+        ncow, short = _i32(), _i32()
+        st = _lib.pa_bm_step(self._h, ids.ctypes.data, b, int(max_blocks_per_seq), bt.ctypes.data, cl.ctypes.data,
+                             sl.ctypes.data, pr.ctypes.data, ctypes.byref(ncow), ctypes.byref(short))
+        if st == PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks("pa_bm_step", short.value)
+        _check(st, "pa_bm_step")
+        return bt[:b], cl[:b], sl[:b], pr[:ncow.value]
 
 
 def pa_timing_enable(every: int = 1) -> None:

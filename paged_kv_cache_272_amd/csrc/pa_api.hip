@@ -143,6 +143,7 @@ PA_EXPORT const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_MISALIGNED: return "a q/out/cache pointer is not 16-byte aligned";
     case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case PA_ERR_OUT_OF_BLOCKS: return "the block pool cannot hold the request";
     default: return "unknown status";
   }
 }

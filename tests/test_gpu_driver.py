@@ -1,0 +1,102 @@
+"""GPU parity of the continuous-batching driver (native block manager + copy
++ fused decode) against a CPU shadow run of the oracle: the oracle's block
+manager, slot scatter, block copy and decode, step by step, with sequences
+joining, forking, finishing and being preempted when the pool runs out."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, log, out_to_f64
+
+pytestmark = pytest.mark.gpu
+pa = pytest.importorskip("paged_kv_cache_272_amd")
+from paged_kv_cache_272_amd.driver import DecodeDriver  # noqa: E402
+
+HQ, HKV, D, NB, MB = 8, 2, 64, 20, 12
+
+
+def _bf16_bits(rng, shape):
+    x = (rng.standard_normal(shape).astype(np.float32) * np.float32(0.5))
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _dev(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_driver_matches_oracle_shadow():
+    rng = np.random.default_rng(401)
+    order = rng.permutation(NB).astype(np.int32)
+    drv = DecodeDriver(NB, HQ, HKV, D, MB, max_batch=8, free_order=order)
+    ref = oracle.BlockManagerRef(NB, order)
+    k_pool = np.zeros((NB, HKV, 16, D), np.uint16)
+    v_pool = np.zeros((NB, HKV, 16, D), np.uint16)
+    running, next_id, preempted, forks = [], 0, 0, 0
+
+    def add(seq, n):
+        k, v = _bf16_bits(rng, (n, HKV, D)), _bf16_bits(rng, (n, HKV, D))
+        ref.add(seq, n)                       # raises OutOfBlocks first, before the driver changes
+        drv.add_sequence(seq, _dev(k), _dev(v))
+        table = ref.tables[seq]
+        for i in range(n):
+            k_pool[table[i // 16], :, i % 16] = k[i]
+            v_pool[table[i // 16], :, i % 16] = v[i]
+
+    for it in range(40):
+        # admissions and forks between iterations
+        while len(running) < 6:
+            n = 16 * int(rng.integers(1, 4)) - int(rng.integers(0, 2))   # full or nearly full last blocks
+            try:
+                add(next_id, n)
+            except oracle.block_manager_ref.OutOfBlocks:
+                break
+            running.append(next_id)
+            next_id += 1
+        if it % 7 == 3 and running and len(running) < 8:
+            parent, child = running[0], 10000 + it
+            ref.fork(parent, child)
+            drv.fork(parent, child)
+            running.append(child)
+            forks += 1
+        # one iteration; preempt the newest sequence while the pool is short
+        b = len(running)
+        q = _bf16_bits(rng, (b, HQ, D))
+        kn, vn = _bf16_bits(rng, (b, HKV, D)), _bf16_bits(rng, (b, HKV, D))
+        while True:
+            try:
+                tables, lens, slots, pairs = ref.step(running)
+                break
+            except oracle.block_manager_ref.OutOfBlocks:
+                with pytest.raises(pa.OutOfBlocks):
+                    drv.step(running, _dev(q[:b]), _dev(kn[:b]), _dev(vn[:b]), torch.empty(b, HQ, D, dtype=torch.bfloat16, device="cuda"))
+                victim = running.pop()
+                ref.free_seq(victim)
+                drv.finish(victim)
+                preempted += 1
+                b = len(running)
+        out = torch.empty(b, HQ, D, dtype=torch.bfloat16, device="cuda")
+        drv.step(running, _dev(q[:b]), _dev(kn[:b]), _dev(vn[:b]), out)
+        torch.cuda.synchronize()
+        assert drv.last_pairs == len(pairs)
+        # the oracle's side of the same iteration
+        if pairs:
+            k_pool, v_pool, _, _ = oracle.copy_blocks_ref(k_pool, v_pool, np.array(pairs, np.int32))
+        k_pool, v_pool = oracle.cache_write_ref(k_pool, v_pool, kn[:b], vn[:b], np.array(slots, np.int64), "bf16",
+                                                "bf16")
+        bt = np.zeros((b, MB), np.int32)
+        for i, t in enumerate(tables):
+            bt[i, :len(t)] = t
+            native, _ = drv.bm.table(running[i])
+            assert list(native) == t
+        want = oracle.decode_ref(q[:b], k_pool, v_pool, bt, np.array(lens), D ** -0.5, "bf16", "bf16")
+        err = float(np.abs(out_to_f64(out) - want).max())
+        assert err <= TOL["bf16"], (it, err)
+        # finish some sequences
+        for s in list(running):
+            if rng.random() < 0.15:
+                running.remove(s)
+                ref.free_seq(s)
+                drv.finish(s)
+    log(f"driver: {next_id} sequences admitted, {forks} forks, {preempted} preemptions")
+    assert forks > 0 and preempted > 0
