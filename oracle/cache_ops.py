@@ -12,7 +12,8 @@ import it.
   the write becomes a scatter to slots.  A negative slot means "skip".
   For an fp8 cache each value is stored as the e4m3 code of
   ``float32(x) / float32(scale[block, head])``, rounded to nearest even and
-  saturated at 448.
+  saturated at 448; for an int4 cache as the int4 code of the same
+  quotient (round half to even, clamped to [-8, 7]), two per byte.
 * ``copy_blocks_ref`` is the copy step of copy-on-write: a block shared by
   several sequences is duplicated when one of them diverges
   ("17 · 连续批处理与 PagedAttention" section 三, 写时复制的共享;
@@ -28,7 +29,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f32, e4m3_quantize
+from .formats import bf16_to_f32, e4m3_quantize, int4_quantize
 
 BLOCK = 16
 
@@ -62,23 +63,27 @@ def cache_write_ref(k_cache: np.ndarray, v_cache: np.ndarray, new_k: np.ndarray,
                 raise ValueError("f32/bf16 caches take sources of the same type")
             k_out[blk, :, off, :] = new_k[t]
             v_out[blk, :, off, :] = new_v[t]
-        elif cache_dtype == "fp8":
+        elif cache_dtype in ("fp8", "int4"):
+            quantize = e4m3_quantize if cache_dtype == "fp8" else int4_quantize
             ks = np.asarray(k_scale, dtype=np.float32)[blk][:, None]
             vs = np.asarray(v_scale, dtype=np.float32)[blk][:, None]
-            k_out[blk, :, off, :] = e4m3_quantize(_src_f32(new_k[t], src_dtype), ks)
-            v_out[blk, :, off, :] = e4m3_quantize(_src_f32(new_v[t], src_dtype), vs)
+            k_out[blk, :, off, :] = quantize(_src_f32(new_k[t], src_dtype), ks)
+            v_out[blk, :, off, :] = quantize(_src_f32(new_v[t], src_dtype), vs)
         else:
             raise ValueError(f"unknown cache dtype {cache_dtype}")
     return k_out, v_out
 
 
-def quantize_pool_ref(values: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """e4m3 codes of a float32 pool ``[NB, Hkv, 16, D]`` with scales ``[NB, Hkv]``."""
-    out = np.empty(values.shape, dtype=np.uint8)
+def quantize_pool_ref(values: np.ndarray, scales: np.ndarray, cache_dtype: str = "fp8") -> np.ndarray:
+    """Codes of a float32 pool ``[NB, Hkv, 16, D]`` with scales ``[NB, Hkv]``:
+    e4m3 (``[NB, Hkv, 16, D]`` bytes) or packed int4 (``[NB, Hkv, 16, D/2]``)."""
+    quantize = e4m3_quantize if cache_dtype == "fp8" else int4_quantize
+    width = values.shape[-1] if cache_dtype == "fp8" else values.shape[-1] // 2
+    out = np.empty(values.shape[:-1] + (width,), dtype=np.uint8)
     step = max(1, (1 << 22) // max(1, int(np.prod(values.shape[1:]))))
     for s in range(0, values.shape[0], step):
         e = min(values.shape[0], s + step)
-        out[s:e] = e4m3_quantize(values[s:e], scales[s:e][:, :, None, None])
+        out[s:e] = quantize(values[s:e], scales[s:e][:, :, None, None])
     return out
 
 

@@ -12,10 +12,17 @@ import it; the library's GPU path never does.
   is NaN; there are no infinities, so the largest finite value is
   ``2^8 * 1.75 = 448``.
 
+* int4: a signed integer in [-8, 7] stored offset by 8 as a 4-bit code
+  0..15, two codes per byte: element 2i in the low nibble of byte i,
+  element 2i+1 in the high nibble.  A value x is stored as the code of
+  clamp(round_half_even(float32(x) / float32(scale)), -8, 7).
+
 The pages only name "fp8" as a KV-cache type ("17 · 连续批处理与
 PagedAttention", section 四, the ``kv_cache_dtype`` knob, which is said to
-roughly double the batch); the e4m3 variant, round-to-nearest-even and
-saturation at +-448 are this build's reading of it.
+roughly double the batch) and compare FP16 / FP8 / INT4 KV in an exercise
+("推理优化", section 五, exercise 1: INT4 about 4x the concurrency); the
+e4m3 variant, round-to-nearest-even, saturation at +-448, and the int4
+layout above are this build's reading of them.
 """
 from __future__ import annotations
 
@@ -101,3 +108,38 @@ def e4m3_quantize(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """Code of ``float32(x) / float32(scale)`` (IEEE binary32 division), saturating RNE."""
     q = np.asarray(x, dtype=np.float32) / np.asarray(scale, dtype=np.float32)
     return e4m3_encode(q.astype(np.float32))
+
+
+INT4_MIN, INT4_MAX, INT4_OFFSET = -8, 7, 8
+
+
+def int4_unpack(packed: np.ndarray) -> np.ndarray:
+    """[..., n] bytes -> [..., 2n] codes 0..15 (element 2i = low nibble of byte i)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def int4_pack(codes: np.ndarray) -> np.ndarray:
+    """[..., 2n] codes 0..15 -> [..., n] bytes."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def int4_to_f64(packed: np.ndarray) -> np.ndarray:
+    """Values (code - 8) of packed int4 bytes, unpacked along the last axis."""
+    return int4_unpack(packed).astype(np.float64) - INT4_OFFSET
+
+
+def int4_encode(x: np.ndarray) -> np.ndarray:
+    """Codes of float32 values: round half to even, clamp to [-8, 7], offset by 8."""
+    r = np.rint(np.asarray(x, dtype=np.float32).astype(np.float64))   # np.rint: half to even
+    return (np.clip(r, INT4_MIN, INT4_MAX) + INT4_OFFSET).astype(np.uint8)
+
+
+def int4_quantize(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Packed codes of ``float32(x) / float32(scale)`` (IEEE binary32 division)."""
+    q = np.asarray(x, dtype=np.float32) / np.asarray(scale, dtype=np.float32)
+    return int4_pack(int4_encode(q.astype(np.float32)))

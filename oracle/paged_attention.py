@@ -52,7 +52,7 @@ from typing import Iterable, Optional, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_to_f64
+from .formats import bf16_to_f64, e4m3_to_f64, int4_to_f64
 
 BLOCK = 16
 
@@ -65,6 +65,8 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_to_f64(x)
     if dtype == "fp8":
         return e4m3_to_f64(x)
+    if dtype == "int4":
+        return int4_to_f64(x)                    # unpacks the last axis: D/2 bytes -> D values
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -88,7 +90,7 @@ def gather_kv(cache: np.ndarray, block_table: np.ndarray, ctx: int, kv_dtype: st
     blocks = to_f64(cache[phys], kv_dtype)                  # [n, Hkv, 16, D]
     if scales is not None:
         blocks = blocks * np.asarray(scales, dtype=np.float32)[phys].astype(np.float64)[:, :, None, None]
-    hkv, d = cache.shape[1], cache.shape[3]
+    hkv, d = blocks.shape[1], blocks.shape[3]
     contiguous = blocks.transpose(1, 0, 2, 3).reshape(hkv, n * BLOCK, d)
     return contiguous[:, :ctx, :]
 
@@ -128,8 +130,8 @@ def decode_ref(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_ta
     q: [B, Hq, D]; caches [NB, Hkv, 16, D]; block_tables [B, MB];
     context_lens [B].  Returns float64 out [len(seqs), Hq, D] (and lse).
     """
-    if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
-        raise ValueError("fp8 caches need k_scale and v_scale")
+    if kv_dtype in ("fp8", "int4") and (k_scale is None or v_scale is None):
+        raise ValueError("fp8 and int4 caches need k_scale and v_scale")
     seqs = list(range(len(context_lens))) if seqs is None else list(seqs)
     hq, d = q.shape[1], q.shape[2]
     outs = np.zeros((len(seqs), hq, d), dtype=np.float64)
@@ -220,8 +222,8 @@ def multi_query_ref(q: np.ndarray, q_start: np.ndarray, k_cache: np.ndarray, v_c
     Token i of sequence b sees positions [0, ctx - q_len + i].  Returns
     float64 [T, Hq, D] (rows of sequences outside ``seqs`` stay zero).
     """
-    if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
-        raise ValueError("fp8 caches need k_scale and v_scale")
+    if kv_dtype in ("fp8", "int4") and (k_scale is None or v_scale is None):
+        raise ValueError("fp8 and int4 caches need k_scale and v_scale")
     q_start = np.asarray(q_start, dtype=np.int64)
     n_seq = len(context_lens)
     if len(q_start) != n_seq + 1 or np.any(np.diff(q_start) < 0) or q_start[0] != 0:

@@ -530,6 +530,60 @@ def check_multi_query_chunking_and_decode():
             assert np.array_equal(one[0], whole[q_start[b] + i]), f"token {i} of sequence {b} != decode"
 
 
+# ---------------------------------------------------------------------------
+# int4 KV
+
+def check_int4_encode_bruteforce():
+    """Nearest of the 16 levels -8..7, ties to the even level, clamped; every tie point tried."""
+    xs = np.concatenate([np.arange(-10.0, 10.01, 0.25), np.random.default_rng(151).uniform(-12, 12, 500)])
+    codes = fm.int4_encode(xs.astype(np.float32))
+    for x, c in zip(xs.astype(np.float32), codes):
+        levels = np.arange(-8, 8)
+        d = np.abs(levels - float(x))
+        best = levels[d == d.min()]
+        want = best[0] if len(best) == 1 else [v for v in best if v % 2 == 0][0]
+        assert int(c) - 8 == want, (float(x), int(c) - 8, want)
+
+
+def check_int4_layout():
+    """Element 2i is the low nibble of byte i; stored code = value + 8."""
+    assert list(fm.int4_to_f64(np.array([0x1F, 0x80], np.uint8))) == [7.0, -7.0, -8.0, 0.0]
+    codes = np.random.default_rng(152).integers(0, 16, size=(3, 64)).astype(np.uint8)
+    assert np.array_equal(fm.int4_unpack(fm.int4_pack(codes)), codes)
+
+
+def check_int4_decode_vs_sdpa(tol=1e-12):
+    """Decode over an int4 pool equals SDPA on values decoded independently
+    (torch bit operations on the packed bytes, times the scales)."""
+    rng = np.random.default_rng(153)
+    hq, hkv, d, ctxs = 8, 2, 16, [5, 16, 37]
+    nb = sum(-(-c // BLOCK) for c in ctxs) + 2
+    kc = rng.integers(0, 256, size=(nb, hkv, BLOCK, d // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(nb, hkv, BLOCK, d // 2)).astype(np.uint8)
+    ks = rng.uniform(0.05, 0.5, size=(nb, hkv)).astype(np.float32)
+    vs = rng.uniform(0.05, 0.5, size=(nb, hkv)).astype(np.float32)
+    perm = rng.permutation(nb)
+    bt = np.zeros((len(ctxs), max(-(-c // BLOCK) for c in ctxs)), np.int32)
+    k = 0
+    for b, c in enumerate(ctxs):
+        n = -(-c // BLOCK)
+        bt[b, :n] = perm[k:k + n]
+        k += n
+    q = rng.standard_normal((len(ctxs), hq, d)).astype(np.float32)
+    got = pa.decode_ref(q, kc, vc, bt, np.array(ctxs), d ** -0.5, "f32", "int4", ks, vs)
+
+    def torch_values(cache, scales, table, ctx):
+        t = torch.from_numpy(cache[table[:-(-ctx // BLOCK)]].astype(np.int64))
+        lo, hi = (t & 15) - 8, (t >> 4) - 8
+        vals = torch.stack([lo, hi], dim=-1).reshape(t.shape[:-1] + (d,)).double()
+        vals = vals * torch.from_numpy(scales[table[:-(-ctx // BLOCK)]].astype(np.float64))[:, :, None, None]
+        return vals.permute(1, 0, 2, 3).reshape(hkv, -1, d)[:, :ctx].numpy()
+
+    for b, c in enumerate(ctxs):
+        want = sdpa_f64(q[b], torch_values(kc, ks, bt[b], c), torch_values(vc, vs, bt[b], c), d ** -0.5)
+        assert np.abs(got[b] - want).max() < tol
+
+
 ALL_CHECKS = [
     check_decode_vs_sdpa, check_decode_vs_python_bruteforce, check_permutation_invariance,
     check_shared_prefix_equivalence, check_special_cases, check_lse, check_partition_merge,
@@ -537,5 +591,6 @@ ALL_CHECKS = [
     check_e4m3_encode_vs_torch, check_e4m3_quantize_division, check_bf16_vs_torch,
     check_fp8_scaled_decode, check_cache_write_vs_contiguous_append, check_copy_blocks,
     check_multi_query_full_prefill_vs_sdpa_causal, check_multi_query_vs_python_bruteforce,
-    check_multi_query_chunking_and_decode,
+    check_multi_query_chunking_and_decode, check_int4_encode_bruteforce, check_int4_layout,
+    check_int4_decode_vs_sdpa,
 ]

@@ -133,6 +133,26 @@ def _positions_no_causal_mask(ctx, q_len):
     return np.full(q_len, ctx - 1, dtype=np.int64)
 
 
+_real_unpack = fm.int4_unpack
+
+
+def _unpack_high_first(packed):
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b >> 4
+    out[..., 1::2] = b & 0x0F
+    return out
+
+
+def _int4_offset_7(packed):
+    return _real_unpack(packed).astype(np.float64) - 7
+
+
+def _int4_encode_truncating(x):
+    t = np.trunc(np.asarray(x, dtype=np.float32).astype(np.float64))
+    return (np.clip(t, -8, 7) + 8).astype(np.uint8)
+
+
 MUTANTS = {
     "gqa_modulo_mapping": (pa, "attend", _attend_mutant(gqa="mod")),
     "scale_dropped": (pa, "attend", _attend_mutant(use_scale=False)),
@@ -152,6 +172,9 @@ MUTANTS = {
     "query_position_off_by_one": (pa, "query_positions", _positions_off_by_one),
     "causal_mask_top_left": (pa, "query_positions", _positions_top_left),
     "causal_mask_missing": (pa, "query_positions", _positions_no_causal_mask),
+    "int4_nibble_order": (fm, "int4_unpack", _unpack_high_first),
+    "int4_offset_7": (fm, "int4_to_f64", _int4_offset_7),
+    "int4_truncating": (fm, "int4_encode", _int4_encode_truncating),
 }
 
 
