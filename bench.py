@@ -50,6 +50,7 @@ KERNELS = {
     "decode_8b": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
     "decode_70b": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
     "long_ctx_fp8": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
+    "decode_8b_int4": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
     "shared_prefix_32x8": ("attend_planned_kernel", PLANNED_SOURCES),
     "verify4_8b": ("attend_planned_kernel", PLANNED_SOURCES),
     "chunked_prefill": ("attend_planned_kernel", PLANNED_SOURCES),
@@ -214,7 +215,13 @@ def _dev(torch, np, a, kind=None):
 def build_decode(args, pa, torch, np, W, oracle, name):
     """Decode workloads: one new token per sequence (pa_decode_append, or
     pa_cache_write + pa_decode with --step separate)."""
-    wl = {"decode_8b": W.config2, "decode_70b": W.config3, "long_ctx_fp8": W.config5}[name]()
+    def int4_8b():
+        base = W.config2(with_values=False)
+        return W.make_workload(name="llama3_8b_int4", seed=2, context_lens=[int(c) for c in base.context_lens],
+                               num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="int4",
+                               fp8_mode="codes")
+    wl = {"decode_8b": W.config2, "decode_70b": W.config3, "long_ctx_fp8": W.config5,
+          "decode_8b_int4": int4_8b}[name]()
     kv = wl.kv_dtype
     q = _dev(torch, np, wl.q, "bf16")
     new_k, new_v = _dev(torch, np, wl.new_k, "bf16"), _dev(torch, np, wl.new_v, "bf16")
@@ -238,15 +245,17 @@ def build_decode(args, pa, torch, np, W, oracle, name):
             steps.append((pa.prepare_cache_write(new_k, new_v, kc, vc, slots, ks, vs),
                           pa.prepare_decode(out, q, kc, vc, bt, cl, wl.max_context_len, wl.scale, ks, vs,
                                             partition_tokens=args.partition_tokens, workspace=ws)))
-    eb = 1 if kv == "fp8" else 2
-    decode_bytes = oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                                   eb, 2, 2, fp8_scales=kv == "fp8")
-    write_bytes = wl.num_seqs * wl.num_kv_heads * wl.head_dim * (2 + eb) * 2 + wl.num_seqs * 8
+    eb = {"fp8": 1, "int4": 0.5}.get(kv, 2)
+    scaled = kv in ("fp8", "int4")
+    decode_bytes = int(oracle.decode_algorithmic_bytes(wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                                                       wl.head_dim, eb, 2, 2, fp8_scales=scaled))
+    write_bytes = int(wl.num_seqs * wl.num_kv_heads * wl.head_dim * (2 + eb) * 2 + wl.num_seqs * 8)
     part = pa.pa_decode_partition_tokens(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                          wl.max_context_len, args.partition_tokens)
     labels = {"decode_8b": ("llama3_8b_shape_decode_bs64", "U{128..4096}"),
               "decode_70b": ("llama3_70b_shape_decode_bs256", "lognormal median 2048 in [16, 8192]"),
-              "long_ctx_fp8": ("llama3_70b_shape_fp8_decode_bs8_ctx131072", "131072 each")}[name]
+              "long_ctx_fp8": ("llama3_70b_shape_fp8_decode_bs8_ctx131072", "131072 each"),
+              "decode_8b_int4": ("llama3_8b_shape_int4_decode_bs64", "U{128..4096}")}[name]
     k_ref = v_ref = None
 
     def cpu_prepare():
@@ -258,14 +267,16 @@ def build_decode(args, pa, torch, np, W, oracle, name):
         oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
                           wl.k_scale, wl.v_scale, seqs=[b])
         return oracle.decode_algorithmic_bytes(wl.context_lens[b:b + 1], wl.num_q_heads, wl.num_kv_heads,
-                                               wl.head_dim, eb, 2, 2, fp8_scales=kv == "fp8")
+                                               wl.head_dim, eb, 2, 2, fp8_scales=scaled)
 
     return Bench(
         workload=labels[0], steps=steps, pools=len(pools), step_bytes=decode_bytes + write_bytes,
-        kernel_bytes=decode_bytes, kernel_flops=None, num_seqs=wl.num_seqs, dtype="bf16" if kv == "bf16" else "fp8",
+        kernel_bytes=decode_bytes, kernel_flops=None, num_seqs=wl.num_seqs, dtype="bf16" if kv == "bf16" else kv,
         kernel_label="decode partition kernel",
         data=("synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)" if kv == "bf16" else
-              "synthetic (seeded bf16 q, random finite e4m3 codes with per-(block, head) scales 2^U(-8,-6))"),
+              "synthetic (seeded bf16 q, random finite e4m3 codes with per-(block, head) scales 2^U(-8,-6))"
+              if kv == "fp8" else
+              "synthetic (seeded bf16 q, random int4 codes with per-(block, head) scales 2^U(-4,-2))"),
         config={"workload": labels[0], "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                 "head_dim": wl.head_dim, "block_size": 16, "context_lens": labels[1],
                 "sum_context": int(wl.context_lens.sum()), "kv_dtype": kv, "pool_blocks": wl.num_blocks,
@@ -365,6 +376,7 @@ def build_planned(args, pa, torch, np, W, oracle, name):
 
 
 WORKLOADS = {"decode_8b": build_decode, "decode_70b": build_decode, "long_ctx_fp8": build_decode,
+             "decode_8b_int4": build_decode,
              "shared_prefix_32x8": build_planned, "verify4_8b": build_planned, "chunked_prefill": build_planned}
 
 

@@ -36,6 +36,15 @@
  * The fp8 type is OCP e4m3 ("E4M3FN": bias 7, max 448, no infinities),
  * gfx950's native 8-bit float.  The pages name "fp8" only as a KV-cache
  * setting ("17 · 连续批处理与 PagedAttention", section 四).
+ *
+ * The int4 type stores a signed integer in [-8, 7] as the 4-bit code
+ * value + 8, two per byte (element 2i in the low nibble of byte i), so an
+ * int4 cache is [num_blocks, kv_heads, 16, head_dim / 2] bytes; values are
+ * code - 8 times the (block, head) scale, and a write stores
+ * clamp(round_half_even(x / scale), -8, 7).  The pages compare FP16, FP8
+ * and INT4 KV caches ("推理优化", section 五, exercise 1).  Wherever this
+ * header says "FP8_E4M3 with k_scale/v_scale", INT4 works the same way
+ * (with head_dim 128).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -52,7 +61,8 @@ extern "C" {
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_BF16 = 1,
-  PA_DTYPE_FP8_E4M3 = 2
+  PA_DTYPE_FP8_E4M3 = 2,
+  PA_DTYPE_INT4 = 3        /* caches only: value + 8 in 4 bits, two per byte; head_dim 128 */
 } pa_dtype;
 
 typedef enum pa_status {

@@ -134,8 +134,10 @@ def int4_to_f64(packed: np.ndarray) -> np.ndarray:
 
 
 def int4_encode(x: np.ndarray) -> np.ndarray:
-    """Codes of float32 values: round half to even, clamp to [-8, 7], offset by 8."""
+    """Codes of float32 values: round half to even, clamp to [-8, 7], offset by 8
+    (NaN, which has no int4 code, takes the code of -8)."""
     r = np.rint(np.asarray(x, dtype=np.float32).astype(np.float64))   # np.rint: half to even
+    r = np.where(np.isnan(r), INT4_MIN, r)
     return (np.clip(r, INT4_MIN, INT4_MAX) + INT4_OFFSET).astype(np.uint8)
 
 

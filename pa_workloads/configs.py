@@ -10,9 +10,10 @@ the attention arithmetic and no format conversion beyond drawing bits:
 * bf16 values are drawn i.i.d. from a 65536-entry table of N(0,1)*sigma
   float32 samples cut to their upper 16 bits (random data needs no rounding
   rule);
-* fp8-e4m3 pools are either drawn directly as random finite codes with
+* fp8-e4m3 and int4 pools are either drawn directly as random codes with
   random per-(block, kv head) scales (``fp8_mode="codes"``), or returned as
-  float32 values plus per-(block, kv head) scales (``fp8_mode="values"``)
+  float32 values plus per-(block, kv head) scales (``fp8_mode="values"``;
+  amax/448 for e4m3, amax/7 for int4)
   for a quantiser to turn into codes;
 * every byte the decode must not read is NaN: unused pool blocks, slots of a
   last block past the context, block-table padding (which points at an
@@ -41,8 +42,10 @@ F32_NAN_BITS = np.uint32(0x7FC00000)
 BF16_NAN_BITS = np.uint16(0x7FC0)
 FP8_NAN_CODE = np.uint8(0x7F)
 
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "int4": np.uint8}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
+# int4 has no NaN: bytes the decode must not read hold code 15 (value 7) in both nibbles
+INT4_POISON = np.uint8(0xFF)
 
 
 @dataclass
@@ -134,6 +137,8 @@ def _nan_like(dtype: str):
         return F32_NAN_BITS.view(np.float32)
     if dtype == "bf16":
         return BF16_NAN_BITS
+    if dtype == "int4":
+        return INT4_POISON
     return FP8_NAN_CODE
 
 
@@ -183,8 +188,9 @@ def _poison(cache: np.ndarray, nan, used_blocks: np.ndarray, tables, context_len
         cache[s // BLOCK_SIZE, :, s % BLOCK_SIZE, :] = nan
 
 
-def _fp8_scales_from_values(values: np.ndarray, tables, context_lens) -> np.ndarray:
-    """Per-(block, kv head) scale = amax/448 over the block's live tokens (recipe)."""
+def _fp8_scales_from_values(values: np.ndarray, tables, context_lens, top: float = 448.0) -> np.ndarray:
+    """Per-(block, kv head) scale = amax/top over the block's live tokens (recipe;
+    top = 448 for e4m3, 7 for int4)."""
     nb, hkv = values.shape[:2]
     scale = np.ones((nb, hkv), dtype=np.float32)
     for b, c in enumerate(context_lens):
@@ -192,7 +198,7 @@ def _fp8_scales_from_values(values: np.ndarray, tables, context_lens) -> np.ndar
         for i, blk in enumerate(tables[b]):
             n = min(BLOCK_SIZE, c - i * BLOCK_SIZE)
             amax = np.abs(values[blk, :, :n, :]).reshape(hkv, -1).max(axis=1)
-            scale[blk] = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0))
+            scale[blk] = np.where(amax > 0, amax / np.float32(top), np.float32(1.0))
     return scale
 
 
@@ -241,13 +247,21 @@ def make_workload(*, name: str, seed: int, context_lens: Sequence[int], num_q_he
     elif kv_dtype == "bf16":
         k_cache = _draw_bf16(rng, table16, (nb, Hkv, BLOCK_SIZE, D))
         v_cache = _draw_bf16(rng, table16, (nb, Hkv, BLOCK_SIZE, D))
+    elif kv_dtype == "int4" and fp8_mode == "codes":
+        # every byte is a valid pair of int4 codes; scales 2^U(-4,-2): values up to 8/4 = 2
+        k_cache = np.frombuffer(rng.bytes(nb * Hkv * BLOCK_SIZE * D // 2), dtype=np.uint8).copy().reshape(
+            nb, Hkv, BLOCK_SIZE, D // 2)
+        v_cache = np.frombuffer(rng.bytes(nb * Hkv * BLOCK_SIZE * D // 2), dtype=np.uint8).copy().reshape(
+            nb, Hkv, BLOCK_SIZE, D // 2)
+        k_scale = np.exp2(rng.uniform(-4.0, -2.0, size=(nb, Hkv))).astype(np.float32)
+        v_scale = np.exp2(rng.uniform(-4.0, -2.0, size=(nb, Hkv))).astype(np.float32)
     elif kv_dtype == "fp8" and fp8_mode == "codes":
         k_cache = _draw_fp8_codes(rng, (nb, Hkv, BLOCK_SIZE, D))
         v_cache = _draw_fp8_codes(rng, (nb, Hkv, BLOCK_SIZE, D))
         # scales 2^u, u ~ U(-8, -6): dequantised magnitudes up to 448/64 = 7
         k_scale = np.exp2(rng.uniform(-8.0, -6.0, size=(nb, Hkv))).astype(np.float32)
         v_scale = np.exp2(rng.uniform(-8.0, -6.0, size=(nb, Hkv))).astype(np.float32)
-    elif kv_dtype == "fp8" and fp8_mode == "values":
+    elif kv_dtype in ("fp8", "int4") and fp8_mode == "values":
         k_values = _draw_f32(rng, sigma, (nb, Hkv, BLOCK_SIZE, D))
         v_values = _draw_f32(rng, sigma, (nb, Hkv, BLOCK_SIZE, D))
         k_cache = v_cache = None
@@ -256,9 +270,10 @@ def make_workload(*, name: str, seed: int, context_lens: Sequence[int], num_q_he
     # 5: new tokens (in the query's storage type)
     new_k, new_v = _extract_new_tokens(rng, q_dtype, kv_dtype, fp8_mode, sigma, table16,
                                        k_cache, v_cache, k_values, v_values, new_slots, Hkv, D)
-    if kv_dtype == "fp8" and fp8_mode == "values":
-        k_scale = _fp8_scales_from_values(k_values, tables, context_lens)
-        v_scale = _fp8_scales_from_values(v_values, tables, context_lens)
+    if kv_dtype in ("fp8", "int4") and fp8_mode == "values":
+        top = 448.0 if kv_dtype == "fp8" else 7.0
+        k_scale = _fp8_scales_from_values(k_values, tables, context_lens, top)
+        v_scale = _fp8_scales_from_values(v_values, tables, context_lens, top)
     # 6: poison
     used = np.array(sorted({blk for t in tables for blk in t}), dtype=np.int64)
     if k_cache is not None:
@@ -275,7 +290,7 @@ def make_workload(*, name: str, seed: int, context_lens: Sequence[int], num_q_he
         context_lens=np.asarray(context_lens, dtype=np.int32), new_k=new_k, new_v=new_v,
         slot_mapping=new_slots, k_scale=k_scale, v_scale=v_scale, k_values=k_values,
         v_values=v_values, refcount=bm.refcount.copy(), partition_tokens=partition_tokens,
-        meta={"num_blocks": nb, "pad_block": pad, "fp8_mode": fp8_mode if kv_dtype == "fp8" else None,
+        meta={"num_blocks": nb, "pad_block": pad, "fp8_mode": fp8_mode if kv_dtype in ("fp8", "int4") else None,
               "sigma": sigma})
     return wl
 

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT4 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 
@@ -118,6 +118,18 @@ def dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 
+def cache_code(cache: torch.Tensor, head_dim: int) -> int:
+    """dtype code of a K/V pool: a byte pool whose rows hold head_dim / 2 bytes is int4."""
+    if cache.dtype == torch.uint8 and cache.shape[-1] * 2 == head_dim:
+        return PA_DTYPE_INT4
+    return dtype_code(cache)
+
+
+def _row(cache: torch.Tensor, head_dim: int) -> int:
+    """Logical head_dim of a pool (int4 pools hold two values per byte)."""
+    return cache.shape[-1] * 2 if cache_code(cache, head_dim) == PA_DTYPE_INT4 else cache.shape[-1]
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
@@ -140,11 +152,12 @@ def pa_cache_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_ca
     """k, v [T, Hkv, D]; caches [NB, Hkv, 16, D]; slot_mapping [T] int64."""
     if slot_mapping.dtype != torch.int64:
         raise TypeError("slot_mapping must be int64")
-    num_blocks, hkv, bs, d = k_cache.shape
-    if bs != BLOCK_SIZE or tuple(k.shape) != (k.shape[0], hkv, d) or k.shape != v.shape:
+    num_blocks, hkv, bs, _ = k_cache.shape
+    d = k.shape[-1]
+    if bs != BLOCK_SIZE or tuple(k.shape) != (k.shape[0], hkv, _row(k_cache, d)) or k.shape != v.shape:
         raise ValueError("shape mismatch between new K/V and the cache")
     _check(_lib.pa_cache_write(_ptr(k), _ptr(v), dtype_code(k), _ptr(k_cache), _ptr(v_cache),
-                               dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
+                               cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
                                k.shape[0], hkv, d, num_blocks, _stream(stream)), "pa_cache_write")
 
 
@@ -177,8 +190,8 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
     b, hq, d = q.shape
-    num_blocks, hkv, bs, dk = k_cache.shape
-    if bs != BLOCK_SIZE or dk != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
+    num_blocks, hkv, bs, _ = k_cache.shape
+    if bs != BLOCK_SIZE or _row(k_cache, d) != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch among q, out and the caches")
     mb = block_tables.shape[1]
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
@@ -186,7 +199,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
-                          dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
+                          cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
                           _ptr(context_lens), int(max_context_len), b, hq, hkv, d, num_blocks, float(scale),
                           int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
 
@@ -196,8 +209,8 @@ def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, co
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
     b, hq, d = q.shape
-    num_blocks, hkv, bs, dk = k_cache.shape
-    if bs != BLOCK_SIZE or dk != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
+    num_blocks, hkv, bs, _ = k_cache.shape
+    if bs != BLOCK_SIZE or _row(k_cache, d) != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch among q, out and the caches")
     if tuple(k_new.shape) != (b, hkv, d) or k_new.shape != v_new.shape or k_new.dtype != q.dtype:
         raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim] in q's dtype")
@@ -206,7 +219,7 @@ def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, co
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-            dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+            cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), int(max_context_len), b, hq, hkv, d, num_blocks, float(scale), int(partition_tokens),
             _ptr(workspace), ws_bytes, _stream(stream))
     return args, workspace
@@ -226,12 +239,16 @@ def pa_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_
 
 def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor,
                    k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-                   stream=None) -> None:
-    """block_pairs [n, 2] int32 (src, dst)."""
+                   stream=None, head_dim: Optional[int] = None) -> None:
+    """block_pairs [n, 2] int32 (src, dst).  head_dim: needed to recognise an
+    int4 pool (rows of head_dim / 2 bytes)."""
     if block_pairs.dtype != torch.int32:
         raise TypeError("block_pairs must be int32")
     num_blocks, hkv, bs, d = k_cache.shape
-    _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale),
+    code = dtype_code(k_cache)
+    if head_dim is not None:
+        code, d = cache_code(k_cache, head_dim), head_dim
+    _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), code, _ptr(k_scale),
                                _ptr(v_scale), _ptr(block_pairs), block_pairs.shape[0], hkv, d, num_blocks,
                                _stream(stream)), "pa_copy_blocks")
 
@@ -285,7 +302,8 @@ def pa_attend_planned(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     """out, q [T, Hq, D] bf16; block_tables [B, MB] int32 (device); plan: device copy of the plan bytes."""
     if block_tables.dtype != torch.int32:
         raise TypeError("block_tables must be int32")
-    num_blocks, hkv, bs, d = k_cache.shape
+    num_blocks, hkv, bs, _ = k_cache.shape
+    d = _row(k_cache, info.head_dim)
     if bs != BLOCK_SIZE or tuple(q.shape) != (info.num_q_tokens, info.num_q_heads, info.head_dim) \
             or out.shape != q.shape or hkv != info.num_kv_heads or d != info.head_dim:
         raise ValueError("tensor shapes do not match the plan")
@@ -293,7 +311,7 @@ def pa_attend_planned(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_attend_planned(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
-                                  dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                  cache_code(k_cache, info.head_dim), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                   block_tables.shape[1], num_blocks, float(scale), _ptr(plan), ctypes.byref(info),
                                   _ptr(workspace), ws_bytes, _stream(stream)), "pa_attend_planned")
 
@@ -304,8 +322,8 @@ def prepare_attend_planned(out, q, k_cache, v_cache, block_tables, scale, plan, 
     if workspace is None and info.workspace_bytes:
         workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale),
-            _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], num_blocks, float(scale), _ptr(plan),
+    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, info.head_dim),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], num_blocks, float(scale), _ptr(plan),
             ctypes.byref(info), _ptr(workspace), ws_bytes, _stream(stream))
     return PreparedCall("pa_attend_planned", args, (out, q, k_cache, v_cache, block_tables, k_scale, v_scale,
                                                     plan, info, workspace))
@@ -437,8 +455,9 @@ class PreparedCall:
 
 def prepare_cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=None,
                         stream=None) -> PreparedCall:
-    num_blocks, hkv, _, d = k_cache.shape
-    args = (_ptr(k), _ptr(v), dtype_code(k), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+    num_blocks, hkv, _, _ = k_cache.shape
+    d = k.shape[-1]
+    args = (_ptr(k), _ptr(v), dtype_code(k), _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, d),
             _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), k.shape[0], hkv, d, num_blocks, _stream(stream))
     return PreparedCall("pa_cache_write", args, (k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale))
 
@@ -452,7 +471,7 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_con
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+    args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, d),
             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
             int(max_context_len), b, hq, hkv, d, num_blocks, float(scale), int(partition_tokens),
             _ptr(workspace), ws_bytes, _stream(stream))

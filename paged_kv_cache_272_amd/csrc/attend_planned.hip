@@ -27,9 +27,9 @@ namespace {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-template <int D, bool kFp8>
+template <int D, int kFmt>
 struct PlannedPending {
-  BlockRegs<D, kFp8> regs;
+  BlockRegs<D, kFmt> regs;
   int i;              // logical block
   float ks, vs;
 };
@@ -37,7 +37,7 @@ struct PlannedPending {
 // One plan item on one wave (KV head g): stream the item's blocks through
 // kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
 // write the output or the partial records.
-template <int D, bool kFp8, int kTiles>
+template <int D, int kFmt, int kTiles>
 __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, int g, int lane) {
   const int r = lane & 15, c = lane >> 4;
   const int ncols = min(it.ncols, 16 * kTiles);
@@ -48,7 +48,7 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   // this lane's query column in each tile (columns past ncols are zero and see nothing)
   int horizon[kTiles];
   int64_t row[kTiles];
-  HeadState<D, kFp8> hs[kTiles];
+  HeadState<D, kFmt> hs[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     PlanColumn col{0, 0, 0, 0};
@@ -69,27 +69,27 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   // physical ids and fp8 scales of 64 blocks at a time: lane j holds block idbase + j
   int idbase = lo - 64, my_blk = 0;
   float my_ks = 1.0f, my_vs = 1.0f;
-  auto fetch = [&](PlannedPending<D, kFp8>& p, int i) {
+  auto fetch = [&](PlannedPending<D, kFmt>& p, int i) {
     if (i - idbase >= 64) {
       idbase += 64;
       const int bi = idbase + lane;
       my_blk = bi < hi ? clampi(table[bi], 0, a.num_blocks - 1) : 0;
-      if constexpr (kFp8) {
+      if constexpr (kFmt != kFmtBf16) {
         my_ks = bi < hi ? a.k_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
         my_vs = bi < hi ? a.v_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
       }
     }
     const int j = i - idbase;
     p.i = i;
-    if constexpr (kFp8) {
+    if constexpr (kFmt != kFmtBf16) {
       p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), j));
       p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), j));
     } else {
       p.ks = p.vs = 1.0f;
     }
-    load_block<D, kFp8>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(my_blk, j), a.num_kv_heads, g, r, c);
+    load_block<D, kFmt>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(my_blk, j), a.num_kv_heads, g, r, c);
   };
-  auto consume = [&](const PlannedPending<D, kFp8>& p) {
+  auto consume = [&](const PlannedPending<D, kFmt>& p) {
     const int t0 = p.i * kBlockTokens;
     const int valid = min(kBlockTokens, it.kv_len - t0);
     hs[0].step_cols(p.regs, valid, horizon[0] - t0, a.scale_log2 * p.ks, p.vs, c);
@@ -98,7 +98,7 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   };
 
   // software pipeline: the next block's loads are in flight while this one computes
-  PlannedPending<D, kFp8> p0, p1;
+  PlannedPending<D, kFmt> p0, p1;
   if (lo < hi) fetch(p0, lo);
   for (int i = lo; i < hi; i += 2) {
     if (i + 1 < hi) fetch(p1, i + 1);
@@ -114,7 +114,7 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   for (int t = 0; t < kTiles; ++t) {
     if (t > 0 && !second) break;
     const float L = hs[t].total_l();
-    float o[4 * Tile<D, kFp8>::kE];
+    float o[4 * Tile<D, kFmt>::kE];
     hs[t].unpack(o);
     if (16 * t + r >= ncols) continue;
     if (it.rec0 < 0) {
@@ -131,14 +131,14 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
 }
 
 // Workgroup x runs the items of slice x in order, one wave per KV head.
-template <int D, bool kFp8, int kTiles>
+template <int D, int kFmt, int kTiles>
 __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(PlannedArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.y * a.waves_per_wg + wave;
   if (g >= a.num_kv_heads) return;
   const int k0 = clampi(a.wg_start[blockIdx.x], 0, a.num_items);
   const int k1 = clampi(a.wg_start[blockIdx.x + 1], k0, a.num_items);
-  for (int k = k0; k < k1; ++k) run_item<D, kFp8, kTiles>(a, a.items[k], g, lane);
+  for (int k = k0; k < k1; ++k) run_item<D, kFmt, kTiles>(a, a.items[k], g, lane);
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's
@@ -200,18 +200,20 @@ __global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(Pla
 hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
-  const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
-  const bool two = a.max_item_columns > 16;
-#define PA_LAUNCH_PLANNED(D_, F_, T_) \
-  hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, 0, stream, a)
+  const int f = a.cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (a.cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
+  const int tiles = a.max_item_columns > 16 ? 2 : 1;
+#define PA_LAUNCH(D_, F_, T_) hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, 0, stream, a)
+#define PA_LAUNCH_T(D_, F_) do { if (tiles == 2) PA_LAUNCH(D_, F_, 2); else PA_LAUNCH(D_, F_, 1); } while (0)
   if (a.head_dim == 128) {
-    if (fp8) { if (two) PA_LAUNCH_PLANNED(128, true, 2); else PA_LAUNCH_PLANNED(128, true, 1); }
-    else { if (two) PA_LAUNCH_PLANNED(128, false, 2); else PA_LAUNCH_PLANNED(128, false, 1); }
+    if (f == kFmtFp8) PA_LAUNCH_T(128, kFmtFp8);
+    else if (f == kFmtInt4) PA_LAUNCH_T(128, kFmtInt4);
+    else PA_LAUNCH_T(128, kFmtBf16);
   } else {
-    if (fp8) { if (two) PA_LAUNCH_PLANNED(64, true, 2); else PA_LAUNCH_PLANNED(64, true, 1); }
-    else { if (two) PA_LAUNCH_PLANNED(64, false, 2); else PA_LAUNCH_PLANNED(64, false, 1); }
+    if (f == kFmtFp8) PA_LAUNCH_T(64, kFmtFp8);
+    else PA_LAUNCH_T(64, kFmtBf16);
   }
-#undef PA_LAUNCH_PLANNED
+#undef PA_LAUNCH_T
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
 // Block copy: the copy step of copy-on-write ("17 · 连续批处理与
 // PagedAttention", section 三).
 //
-// Both are pure data movement: one workgroup per (token or pair, K or V),
-// 16-byte vector loads and stores, 64-bit address arithmetic.
+// Both are pure data movement (plus the e4m3 or int4 encode of new rows):
+// one workgroup per (token or pair, K or V), vector loads and stores,
+// 64-bit address arithmetic.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -87,6 +88,46 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_fp8_kernel(CacheWri
   }
 }
 
+// Quantise one token's [Hkv, D] row to int4 codes with the destination
+// block's scale: 8 values -> one 32-bit word (element 2i in the low nibble
+// of byte i).
+template <bool kSrcBf16>
+__global__ __launch_bounds__(kWriteThreads) void cache_write_int4_kernel(CacheWriteArgs a) {
+  const int t = blockIdx.x;
+  const bool is_v = blockIdx.y != 0;
+  const int64_t slot = token_slot(a, t);
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * kBlockTokens) return;
+  const int64_t blk = slot / kBlockTokens;
+  const int off = (int)(slot % kBlockTokens);
+  const int row_groups = a.head_dim / 8;                 // groups of 8 values -> one word of codes
+  const int groups = a.num_kv_heads * row_groups;
+  const float* scales = is_v ? a.v_scale : a.k_scale;
+  uint32_t* cache = reinterpret_cast<uint32_t*>(is_v ? a.v_cache : a.k_cache);
+  for (int i = threadIdx.x; i < groups; i += kWriteThreads) {
+    const int h = i / row_groups, c = i % row_groups;
+    float x[8];
+    if constexpr (kSrcBf16) {
+      const uint4 w = reinterpret_cast<const uint4*>(is_v ? a.v : a.k)[(int64_t)t * groups + i];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_bits_to_f32(ws[j] & 0xffffu);
+        x[2 * j + 1] = bf16_bits_to_f32(ws[j] >> 16);
+      }
+    } else {
+      const float4* s4 = reinterpret_cast<const float4*>(is_v ? a.v : a.k) + ((int64_t)t * groups + i) * 2;
+      const float4 lo = s4[0], hi = s4[1];
+      x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+      x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+    }
+    const float s = scales[blk * a.num_kv_heads + h];
+    uint32_t code = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) code |= f32_to_int4_code(__fdiv_rn(x[j], s)) << (4 * j);
+    cache[((blk * a.num_kv_heads + h) * kBlockTokens + off) * row_groups + c] = code;
+  }
+}
+
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArgs a, int block_chunks) {
   const int i = blockIdx.x;
   const bool is_v = blockIdx.y != 0;
@@ -110,6 +151,11 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(cache_write_fp8_kernel<true>, grid, dim3(kWriteThreads), 0, stream, a);
     else
       hipLaunchKernelGGL(cache_write_fp8_kernel<false>, grid, dim3(kWriteThreads), 0, stream, a);
+  } else if (a.cache_dtype == PA_DTYPE_INT4) {
+    if (a.src_dtype == PA_DTYPE_BF16)
+      hipLaunchKernelGGL(cache_write_int4_kernel<true>, grid, dim3(kWriteThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(cache_write_int4_kernel<false>, grid, dim3(kWriteThreads), 0, stream, a);
   } else {
     const int e = a.cache_dtype == PA_DTYPE_F32 ? 4 : 2;
     hipLaunchKernelGGL(cache_write_copy_kernel, grid, dim3(kWriteThreads), 0, stream, a, e);
@@ -118,10 +164,11 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
-  const int e = a.cache_dtype == PA_DTYPE_F32 ? 4 : (a.cache_dtype == PA_DTYPE_BF16 ? 2 : 1);
-  const int block_chunks = a.num_kv_heads * kBlockTokens * a.head_dim * e / 16;
+  const int bits = a.cache_dtype == PA_DTYPE_F32 ? 32 : (a.cache_dtype == PA_DTYPE_BF16 ? 16 :
+                   (a.cache_dtype == PA_DTYPE_INT4 ? 4 : 8));
+  const int block_chunks = a.num_kv_heads * kBlockTokens * a.head_dim * bits / 8 / 16;
   CopyBlocksArgs b = a;
-  if (a.cache_dtype != PA_DTYPE_FP8_E4M3) b.k_scale = b.v_scale = nullptr;
+  if (a.cache_dtype != PA_DTYPE_FP8_E4M3 && a.cache_dtype != PA_DTYPE_INT4) b.k_scale = b.v_scale = nullptr;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2), dim3(kCopyThreads), 0, stream, b,
                      block_chunks);
   return hipGetLastError();

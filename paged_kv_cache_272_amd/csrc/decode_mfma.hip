@@ -35,9 +35,9 @@ __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int b) {
 // Partition grid: one workgroup of 4 waves per (partition, KV head, sequence);
 // wave w takes the partition's blocks w, w+4, ... and the waves merge in LDS.
 
-template <int D, bool kFp8>
+template <int D, int kFmt>
 __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a) {
-  using T = Tile<D, kFp8>;
+  using T = Tile<D, kFmt>;
   constexpr int kE = T::kE;
   __shared__ float lds_m[kPartWaves][16];
   __shared__ float lds_l[kPartWaves][16];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
   const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
   const int nw = wave < nblk ? (nblk - wave + kPartWaves - 1) / kPartWaves : 0;   // blocks of this wave
 
-  HeadState<D, kFp8> hs;
+  HeadState<D, kFmt> hs;
   hs.begin(reinterpret_cast<const uint16_t*>(a.q), head0, G, r, c);
   // physical ids (and fp8 scales) of this wave's blocks: lane j holds block j
   int my_blk = 0;
@@ -73,16 +73,16 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
     my_blk = clamp_block(
         a.block_tables[(int64_t)b * a.max_blocks_per_seq + t0 / kBlockTokens + wave + kPartWaves * lane],
         a.num_blocks);
-    if constexpr (kFp8) {
+    if constexpr (kFmt != kFmtBf16) {
       my_ks = a.k_scale[(int64_t)my_blk * a.num_kv_heads + g];
       my_vs = a.v_scale[(int64_t)my_blk * a.num_kv_heads + g];
     }
   }
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
-  auto step = [&](const BlockRegs<D, kFp8>& br, int i) {
+  auto step = [&](const BlockRegs<D, kFmt>& br, int i) {
     float sc = a.scale_log2, vs = 1.0f;
-    if constexpr (kFp8) {
+    if constexpr (kFmt != kFmtBf16) {
       sc *= __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i));
       vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i));
     }
@@ -91,15 +91,15 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
   };
 
   // software pipeline: the next block's loads are in flight while this one computes
-  BlockRegs<D, kFp8> b0, b1;
-  if (nw > 0) load_block<D, kFp8>(b0, kbase, vbase, __builtin_amdgcn_readlane(my_blk, 0), a.num_kv_heads, g, r, c);
+  BlockRegs<D, kFmt> b0, b1;
+  if (nw > 0) load_block<D, kFmt>(b0, kbase, vbase, __builtin_amdgcn_readlane(my_blk, 0), a.num_kv_heads, g, r, c);
   for (int i = 0; i < nw; i += 2) {
     if (i + 1 < nw)
-      load_block<D, kFp8>(b1, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 1), a.num_kv_heads, g, r, c);
+      load_block<D, kFmt>(b1, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 1), a.num_kv_heads, g, r, c);
     step(b0, i);
     if (i + 1 < nw) {
       if (i + 2 < nw)
-        load_block<D, kFp8>(b0, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 2), a.num_kv_heads, g, r, c);
+        load_block<D, kFmt>(b0, kbase, vbase, __builtin_amdgcn_readlane(my_blk, i + 2), a.num_kv_heads, g, r, c);
       step(b1, i + 1);
     }
   }
@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
     lds_m[wave][r] = hs.m;
     lds_l[wave][r] = lw;
   }
+  hs.settle();
 #pragma unroll
   for (int t = 0; t < kE; ++t) lds_acc[wave][t][lane] = hs.acc[t];
   __syncthreads();
@@ -182,7 +183,7 @@ __device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int
   return lo;
 }
 
-template <bool kFp8>
+template <bool kScaled>
 __device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int g,
                                             int lane) {
   UnitIds id{0, 0, 0, 1.0f, 1.0f};
@@ -191,7 +192,7 @@ __device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* star
     id.b = find_sequence(start, a.num_seqs, u);
     id.i = u - start[id.b];
     id.blk = clamp_block(a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i], a.num_blocks);
-    if constexpr (kFp8) {
+    if constexpr (kScaled) {
       id.ks = a.k_scale[(int64_t)id.blk * a.num_kv_heads + g];
       id.vs = a.v_scale[(int64_t)id.blk * a.num_kv_heads + g];
     }
@@ -199,9 +200,9 @@ __device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* star
   return id;
 }
 
-template <int D, bool kFp8>
+template <int D, int kFmt>
 struct Pending {
-  BlockRegs<D, kFp8> regs;
+  BlockRegs<D, kFmt> regs;
   int64_t blk;
   int b, i;
   float ks, vs;
@@ -210,9 +211,9 @@ struct Pending {
   uint32_t nv[D / 32];      // its V run (lane group c == off / 4) as bf16 pairs
 };
 
-template <int D, bool kFp8>
+template <int D, int kFmt>
 __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_kernel(DecodeArgs a) {
-  constexpr int kE = Tile<D, kFp8>::kE;
+  constexpr int kE = Tile<D, kFmt>::kE;
   extern __shared__ int s_dyn[];                 // start[B + 1], then ctx[B]
   __shared__ int s_wave_tot[kBalancedMaxWaves];
   int* s_start = s_dyn;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
   const int d0 = (D / 4) * c;
 
-  HeadState<D, kFp8> hs;
+  HeadState<D, kFmt> hs;
   int cur_b = -1;
   auto finish = [&](int b) {
     const float L = hs.total_l();
@@ -301,19 +302,19 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
 
   // ids of the current 64-unit chunk and of the next one (kept one chunk ahead)
   int base = u0;
-  UnitIds cur = unit_ids<kFp8>(a, s_start, base, u1, g, lane);
-  UnitIds nxt = unit_ids<kFp8>(a, s_start, base + 64, u1, g, lane);
-  auto fetch = [&](Pending<D, kFp8>& p, int u) {
+  UnitIds cur = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base, u1, g, lane);
+  UnitIds nxt = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base + 64, u1, g, lane);
+  auto fetch = [&](Pending<D, kFmt>& p, int u) {
     if (u - base >= 64) {
       base += 64;
       cur = nxt;
-      nxt = unit_ids<kFp8>(a, s_start, base + 64, u1, g, lane);
+      nxt = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base + 64, u1, g, lane);
     }
     const int j = u - base;
     p.b = __builtin_amdgcn_readlane(cur.b, j);
     p.i = __builtin_amdgcn_readlane(cur.i, j);
     p.blk = __builtin_amdgcn_readlane(cur.blk, j);
-    if constexpr (kFp8) {
+    if constexpr (kFmt != kFmtBf16) {
       p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
       p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
     } else {
@@ -334,28 +335,30 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
                            p.nv);
       }
     }
-    load_block<D, kFp8>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
+    load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
   };
   // Appending: put the newest token's K/V row into the block this wave holds
   // and into its slot in the cache (the wave that reads a block is the only
   // reader of that slot in this launch).
-  auto splice = [&](Pending<D, kFp8>& p) {
-    using T = Tile<D, kFp8>;
+  auto splice = [&](Pending<D, kFmt>& p) {
+    using T = Tile<D, kFmt>;
     const int64_t head_base = (p.blk * a.num_kv_heads + g) * kBlockTokens;
     uint8_t* kw = const_cast<uint8_t*>(kbase);
     uint8_t* vw = const_cast<uint8_t*>(vbase);
     if (r == p.off) {
       uint32_t words[T::kKWords];
-      if constexpr (kFp8) quantize_bf16_words<D / 4>(p.nk, p.ks, words);
+      if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 4>(p.nk, p.ks, words);
+      else if constexpr (kFmt == kFmtInt4) quantize_bf16_words_int4<D / 4>(p.nk, p.ks, words);
       else
 #pragma unroll
         for (int w = 0; w < T::kKWords; ++w) words[w] = p.nk[w];
 #pragma unroll
       for (int w = 0; w < T::kKWords; ++w) p.regs.k[w] = words[w];
-      store_words<T::kKWords>(kw + ((head_base + r) * D + d0) * T::kEb, words);
+      store_words<T::kKWords>(kw + T::bytes((head_base + r) * D + d0), words);
     }
     uint32_t words[T::kVWords];
-    if constexpr (kFp8) quantize_bf16_words<D / 16>(p.nv, p.vs, words);
+    if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 16>(p.nv, p.vs, words);
+    else if constexpr (kFmt == kFmtInt4) quantize_bf16_words_int4<D / 16>(p.nv, p.vs, words);
     else
 #pragma unroll
       for (int w = 0; w < T::kVWords; ++w) words[w] = p.nv[w];
@@ -366,9 +369,9 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
 #pragma unroll
       for (int w = 0; w < T::kVWords; ++w) p.regs.v[ee][w] = hit ? words[w] : p.regs.v[ee][w];
     }
-    if (c == p.off / 4) store_words<T::kVWords>(vw + ((head_base + p.off) * D + T::kE * r) * T::kEb, words);
+    if (c == p.off / 4) store_words<T::kVWords>(vw + T::bytes((head_base + p.off) * D + T::kE * r), words);
   };
-  auto consume = [&](Pending<D, kFp8>& p) {
+  auto consume = [&](Pending<D, kFmt>& p) {
     if (p.b != cur_b) {
       if (cur_b >= 0) finish(cur_b);
       cur_b = p.b;
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
     hs.step(p.regs, valid, a.scale_log2 * p.ks, p.vs, c);
   };
 
-  Pending<D, kFp8> p0, p1;
+  Pending<D, kFmt> p0, p1;
   fetch(p0, u0);
   for (int u = u0; u < u1; u += 2) {
     if (u + 1 < u1) fetch(p1, u + 1);
@@ -455,16 +458,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_balanced_kernel(De
 
 }  // namespace
 
+namespace {
+
+int kv_format(pa_dtype cache_dtype) {
+  return cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
+}
+
+}  // namespace
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-  const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
+  const int f = kv_format(a.cache_dtype);
+#define PA_LAUNCH(D_, F_) hipLaunchKernelGGL((decode_mfma_kernel<D_, F_>), grid, dim3(kPartThreads), 0, stream, a)
   if (a.head_dim == 128) {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, dim3(kPartThreads), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, dim3(kPartThreads), 0, stream, a);
+    if (f == kFmtFp8) PA_LAUNCH(128, kFmtFp8);
+    else if (f == kFmtInt4) PA_LAUNCH(128, kFmtInt4);
+    else PA_LAUNCH(128, kFmtBf16);
   } else {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, dim3(kPartThreads), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, dim3(kPartThreads), 0, stream, a);
+    if (f == kFmtFp8) PA_LAUNCH(64, kFmtFp8);
+    else PA_LAUNCH(64, kFmtBf16);
   }
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 
@@ -472,14 +486,17 @@ hipError_t launch_decode_mfma_balanced(const DecodeArgs& a, hipStream_t stream) 
   const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
   const size_t lds = (2 * (size_t)a.num_seqs + 1) * sizeof(int);
-  const bool fp8 = a.cache_dtype == PA_DTYPE_FP8_E4M3;
+  const int f = kv_format(a.cache_dtype);
+#define PA_LAUNCH(D_, F_) hipLaunchKernelGGL((decode_mfma_balanced_kernel<D_, F_>), grid, block, lds, stream, a)
   if (a.head_dim == 128) {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_balanced_kernel<128, true>), grid, block, lds, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<128, false>), grid, block, lds, stream, a);
+    if (f == kFmtFp8) PA_LAUNCH(128, kFmtFp8);
+    else if (f == kFmtInt4) PA_LAUNCH(128, kFmtInt4);
+    else PA_LAUNCH(128, kFmtBf16);
   } else {
-    if (fp8) hipLaunchKernelGGL((decode_mfma_balanced_kernel<64, true>), grid, block, lds, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<64, false>), grid, block, lds, stream, a);
+    if (f == kFmtFp8) PA_LAUNCH(64, kFmtFp8);
+    else PA_LAUNCH(64, kFmtBf16);
   }
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 

@@ -69,14 +69,40 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks) {
   return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
 }
 
-template <int D, bool kFp8>
+// KV storage formats: bf16 values; e4m3 codes with per-(block, head) scales;
+// int4 codes (value + 8, two per byte, element 2i in the low nibble) with
+// per-(block, head) scales.
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtInt4 = 2;
+
+template <int D, int kFmt>
 struct Tile {
   static constexpr int kKSteps = D / 32;                  // QK MFMAs (16x16x32)
   static constexpr int kE = D / 16;                       // V elements per lane per token = PV MFMAs
-  static constexpr int kEb = kFp8 ? 1 : 2;
-  static constexpr int kKWords = kKSteps * 8 * kEb / 4;   // K words per lane per block
-  static constexpr int kVWords = kE * kEb / 4;            // V words per lane per token
+  static constexpr int kBits = kFmt == kFmtBf16 ? 16 : (kFmt == kFmtFp8 ? 8 : 4);
+  static constexpr int kKWords = kKSteps * 8 * kBits / 32;   // K words per lane per block
+  static constexpr int kVWords = kE * kBits / 32;            // V words per lane per token
+  static constexpr bool kScaled = kFmt != kFmtBf16;
+  static_assert(kVWords >= 1, "int4 needs head_dim 128");
+  // byte offset of element `e` of the pool
+  static __device__ __forceinline__ int64_t bytes(int64_t e) { return e * kBits / 8; }
 };
+
+// int4 code c (value c - 8) -> bf16 bits of 128 + c = value + 136, exactly
+// (bf16 holds every integer up to 256).  A dot product over such values is
+// the true one plus 136 times the sum of the other operand.
+constexpr float kInt4Bias = 136.0f;
+
+// 8 int4 codes (one word, element 2i in the low nibble of byte i) -> 4 words
+// of bf16 pairs (elements 2i, 2i+1 in word i).
+__device__ __forceinline__ void int4x8_to_bf16x8(uint32_t w, uint32_t* out) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // byte i of lo -> bits 0-7, byte i of hi -> bits 16-23, zeros elsewhere
+    const uint32_t sel = (uint32_t)i | 0x0c00u | ((uint32_t)(4 + i) << 16) | 0x0c000000u;
+    out[i] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+  }
+}
 
 // Load `W` 32-bit words from a 4*W-byte aligned address.
 template <int W>
@@ -128,32 +154,52 @@ __device__ __forceinline__ void quantize_bf16_words(const uint32_t* src, float s
   }
 }
 
+// NV bf16 values (NV/2 words) -> NV int4 codes (NV/8 words) of x / scale,
+// IEEE division, round half to even, clamped to [-8, 7] (as the slot scatter does).
+template <int NV>
+__device__ __forceinline__ void quantize_bf16_words_int4(const uint32_t* src, float scale, uint32_t* dst) {
+#pragma unroll
+  for (int i = 0; i < NV / 8; ++i) {
+    uint32_t code = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int v = 8 * i + k;
+      const uint32_t bits = (v & 1) ? (src[v / 2] >> 16) : (src[v / 2] & 0xffffu);
+      code |= f32_to_int4_code(__fdiv_rn(bf16_bits_to_f32(bits), scale)) << (4 * k);
+    }
+    dst[i] = code;
+  }
+}
+
 // One 16-token K/V block of one KV head, as this lane holds it.
-template <int D, bool kFp8>
+template <int D, int kFmt>
 struct BlockRegs {
-  uint32_t k[Tile<D, kFp8>::kKWords];
-  uint32_t v[4][Tile<D, kFp8>::kVWords];
+  uint32_t k[Tile<D, kFmt>::kKWords];
+  uint32_t v[4][Tile<D, kFmt>::kVWords];
 };
 
-template <int D, bool kFp8>
-__device__ __forceinline__ void load_block(BlockRegs<D, kFp8>& br, const uint8_t* kbase, const uint8_t* vbase,
+template <int D, int kFmt>
+__device__ __forceinline__ void load_block(BlockRegs<D, kFmt>& br, const uint8_t* kbase, const uint8_t* vbase,
                                            int64_t blk, int num_kv_heads, int g, int r, int c) {
-  using T = Tile<D, kFp8>;
+  using T = Tile<D, kFmt>;
   const int64_t head_base = (blk * num_kv_heads + g) * kBlockTokens;            // token row index
-  load_words<T::kKWords>(kbase + ((head_base + r) * D + (D / 4) * c) * T::kEb, br.k);
+  load_words<T::kKWords>(kbase + T::bytes((head_base + r) * D + (D / 4) * c), br.k);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    load_words<T::kVWords>(vbase + ((head_base + 4 * c + e) * D + T::kE * r) * T::kEb, br.v[e]);
+    load_words<T::kVWords>(vbase + T::bytes((head_base + 4 * c + e) * D + T::kE * r), br.v[e]);
 }
 
 // Running state of one wave: G query heads of one KV head over a run of blocks.
-template <int D, bool kFp8>
+template <int D, int kFmt>
 struct HeadState {
-  using T = Tile<D, kFp8>;
+  using T = Tile<D, kFmt>;
   static constexpr int kE = T::kE;
+  static constexpr bool kInt4 = kFmt == kFmtInt4;
   bf16x8_t qop[T::kKSteps];
   f32x4_t acc[kE];
   float m, l;
+  float qbias;   // int4: 136 * (sum of this lane's query column): removed from every logit
+  float vbias;   // int4: sum over blocks of V scale * (sum of the block's bf16 P), rescaled like acc
 
   // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
   __device__ __forceinline__ void begin(const uint16_t* q, int64_t q_row0, int G, int r, int c) {
@@ -165,6 +211,7 @@ struct HeadState {
       qop[i] = __builtin_bit_cast(bf16x8_t, w);
     }
     reset();
+    set_qbias();
   }
 
   // Q^T operand with an arbitrary query row per column: lane r takes row
@@ -178,11 +225,26 @@ struct HeadState {
       qop[i] = __builtin_bit_cast(bf16x8_t, w);
     }
     reset();
+    set_qbias();
+  }
+
+  // int4: 136 times the column's query sum (the 4 lane groups hold D/4 each)
+  __device__ __forceinline__ void set_qbias() {
+    qbias = 0.0f;
+    if constexpr (kInt4) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < T::kKSteps; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += (float)qop[i][j];
+      qbias = kInt4Bias * sum_xor16(sum_xor32(s));
+    }
   }
 
   __device__ __forceinline__ void reset() {
     m = -INFINITY;
     l = 0.0f;
+    vbias = 0.0f;
 #pragma unroll
     for (int t = 0; t < kE; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -190,7 +252,7 @@ struct HeadState {
   // Fold one block in.  `valid` = tokens of the block inside the context
   // (1..16), `sc` = scale*log2(e) (times the block's K scale for e4m3),
   // `vs` = the block's V scale.  Every column sees the same tokens.
-  __device__ __forceinline__ void step(const BlockRegs<D, kFp8>& br, int valid, float sc, float vs, int c) {
+  __device__ __forceinline__ void step(const BlockRegs<D, kFmt>& br, int valid, float sc, float vs, int c) {
     step_impl<false>(br, valid, 0, sc, vs, c);
   }
 
@@ -199,28 +261,36 @@ struct HeadState {
   // <= 0 hides the whole block, >= 16 hides nothing).  `valid` still bounds
   // the tokens whose V rows hold data.  A column may see no token at all
   // (then m stays -inf, l = 0, acc = 0).
-  __device__ __forceinline__ void step_cols(const BlockRegs<D, kFp8>& br, int valid, int col_valid, float sc,
+  __device__ __forceinline__ void step_cols(const BlockRegs<D, kFmt>& br, int valid, int col_valid, float sc,
                                             float vs, int c) {
     step_impl<true>(br, valid, col_valid, sc, vs, c);
   }
 
   template <bool kCols>
-  __device__ __forceinline__ void step_impl(const BlockRegs<D, kFp8>& br, int valid, int col_valid, float sc,
+  __device__ __forceinline__ void step_impl(const BlockRegs<D, kFmt>& br, int valid, int col_valid, float sc,
                                             float vs, int c) {
     // ---- S^T = K . Q^T
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int st = 0; st < T::kKSteps; ++st) {
       uint4 kw;
-      if constexpr (kFp8) {
+      if constexpr (kFmt == kFmtFp8) {
         kw = make_uint4(fp8x2_to_bf16x2(br.k[2 * st], false), fp8x2_to_bf16x2(br.k[2 * st], true),
                         fp8x2_to_bf16x2(br.k[2 * st + 1], false), fp8x2_to_bf16x2(br.k[2 * st + 1], true));
+      } else if constexpr (kInt4) {
+        uint32_t w4[4];
+        int4x8_to_bf16x8(br.k[st], w4);
+        kw = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       } else {
         kw = make_uint4(br.k[4 * st], br.k[4 * st + 1], br.k[4 * st + 2], br.k[4 * st + 3]);
       }
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
     }
-    float sv[4] = {s[0] * sc, s[1] * sc, s[2] * sc, s[3] * sc};
+    // int4: the MFMA saw values + 136; remove 136 * (query sum) before scaling
+    const float sb = -qbias * sc;
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = kInt4 ? __builtin_fmaf(s[j], sc, sb) : s[j] * sc;
     uint32_t vmask = 0xfu;                                        // tokens 4c+e kept for P.V (bit e)
     if (valid < kBlockTokens) {
 #pragma unroll
@@ -244,6 +314,7 @@ struct HeadState {
       const float alpha = kCols ? (m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f)
                                 : __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
+      if constexpr (kInt4) vbias *= alpha;
 #pragma unroll
       for (int t = 0; t < kE; ++t) acc[t] *= alpha;
       m = m_new;
@@ -256,9 +327,15 @@ struct HeadState {
     l += (p[0] + p[1]) + (p[2] + p[3]);
     // e4m3: the block's V scale is applied in fp32 to the block's P.V product
     // (folding it into the bf16 P would put a relative 2^-9 error on every V row)
-    const float pv = kFp8 ? 1.0f : vs;
-    const short4_t pop = __builtin_bit_cast(
-        short4_t, make_uint2(pack_bf16x2(p[0] * pv, p[1] * pv), pack_bf16x2(p[2] * pv, p[3] * pv)));
+    const float pv = T::kScaled ? 1.0f : vs;
+    const uint2 pbits = make_uint2(pack_bf16x2(p[0] * pv, p[1] * pv), pack_bf16x2(p[2] * pv, p[3] * pv));
+    const short4_t pop = __builtin_bit_cast(short4_t, pbits);
+    if constexpr (kInt4) {
+      // the P.V MFMA sees V + 136: keep V scale * (sum of the bf16 P it used) to take off at the end
+      const float ps = (bf16_bits_to_f32(pbits.x & 0xffffu) + bf16_bits_to_f32(pbits.x >> 16)) +
+                       (bf16_bits_to_f32(pbits.y & 0xffffu) + bf16_bits_to_f32(pbits.y >> 16));
+      vbias = __builtin_fmaf(sum_xor16(sum_xor32(ps)), vs, vbias);
+    }
     // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n).  Masked
     // tokens get V = 0 by selection (their slots may hold NaN).
     uint32_t vw[4][T::kVWords];
@@ -269,7 +346,16 @@ struct HeadState {
 #pragma unroll
     for (int nn = 0; nn < kE; ++nn) {
       uint32_t lo, hi;
-      if constexpr (kFp8) {
+      if constexpr (kInt4) {
+        // nibble nn of each of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code
+        const uint32_t sel = (uint32_t)(nn / 2) | 0x0c00u | ((uint32_t)(4 + nn / 2) << 16) | 0x0c000000u;
+        const uint32_t b01 = __builtin_amdgcn_perm(vw[1][0], vw[0][0], sel);
+        const uint32_t b23 = __builtin_amdgcn_perm(vw[3][0], vw[2][0], sel);
+        lo = ((nn & 1) ? (b01 >> 4) : b01) & 0x000f000fu;
+        hi = ((nn & 1) ? (b23 >> 4) : b23) & 0x000f000fu;
+        lo |= 0x43004300u;
+        hi |= 0x43004300u;
+      } else if constexpr (kFmt == kFmtFp8) {
         // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
         const int w = nn / 4, byte = nn % 4;
         const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
@@ -284,7 +370,7 @@ struct HeadState {
         hi = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
       }
       const short4_t vop = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
-      if constexpr (kFp8) {
+      if constexpr (T::kScaled) {
         const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
         acc[nn] += t * vs;
       } else {
@@ -296,12 +382,23 @@ struct HeadState {
   // The wave's total sum (the 4 lane groups hold partial sums of one head).
   __device__ __forceinline__ float total_l() const { return sum_xor16(sum_xor32(l)); }
 
+  // int4: take the V bias out of acc itself (for callers that read acc directly)
+  __device__ __forceinline__ void settle() {
+    if constexpr (kInt4) {
+      const float vb = kInt4Bias * vbias;
+#pragma unroll
+      for (int t = 0; t < kE; ++t) acc[t] -= vb;
+      vbias = 0.0f;
+    }
+  }
+
   // Output run of this lane: d = (D/4)*c + kE*j + n  ->  o[kE*j + n].
   __device__ __forceinline__ void unpack(float* o) const {
+    const float vb = kInt4 ? kInt4Bias * vbias : 0.0f;
 #pragma unroll
     for (int nn = 0; nn < kE; ++nn)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[kE * j + nn] = acc[nn][j];
+      for (int j = 0; j < 4; ++j) o[kE * j + nn] = kInt4 ? acc[nn][j] - vb : acc[nn][j];
   }
 };
 

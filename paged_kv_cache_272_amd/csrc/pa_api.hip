@@ -24,7 +24,11 @@ namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline bool valid_dtype(int d) { return d == PA_DTYPE_F32 || d == PA_DTYPE_BF16 || d == PA_DTYPE_FP8_E4M3; }
+inline bool valid_dtype(int d) {
+  return d == PA_DTYPE_F32 || d == PA_DTYPE_BF16 || d == PA_DTYPE_FP8_E4M3 || d == PA_DTYPE_INT4;
+}
+// caches whose codes are scaled per (block, head)
+inline bool scaled_dtype(int d) { return d == PA_DTYPE_FP8_E4M3 || d == PA_DTYPE_INT4; }
 
 // Automatic partition length: whole sequences when they are short, else
 // 512-token partitions (a multiple of the 16-token block).
@@ -154,15 +158,16 @@ PA_EXPORT int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype, v
                              int32_t head_dim, int32_t num_blocks, void* stream) {
   if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_BAD_SHAPE;
   if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
-  if (cache_dtype == PA_DTYPE_FP8_E4M3) {
-    if (src_dtype == PA_DTYPE_FP8_E4M3) return PA_ERR_BAD_DTYPE;
+  if (scaled_dtype(cache_dtype)) {
+    if (scaled_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
   } else if (src_dtype != cache_dtype) {
     return PA_ERR_BAD_DTYPE;
   }
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (cache_dtype == PA_DTYPE_INT4 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
-  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
   CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, nullptr, nullptr, num_tokens,
                    num_kv_heads, head_dim, num_blocks, 0, src_dtype, cache_dtype};
@@ -208,15 +213,16 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
   const bool combo_ok = (q_dtype == PA_DTYPE_F32 && cache_dtype == PA_DTYPE_F32) ||
                         (q_dtype == PA_DTYPE_BF16 && cache_dtype == PA_DTYPE_BF16) ||
-                        (q_dtype == PA_DTYPE_BF16 && cache_dtype == PA_DTYPE_FP8_E4M3);
+                        (q_dtype == PA_DTYPE_BF16 && scaled_dtype(cache_dtype));
   if (!combo_ok) return PA_ERR_BAD_DTYPE;
+  if (cache_dtype == PA_DTYPE_INT4 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE) return PA_ERR_BAD_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
   if (append && (!k_new || !v_new)) return PA_ERR_NULL_POINTER;
   if (append && (!aligned16(k_new) || !aligned16(v_new))) return PA_ERR_MISALIGNED;
-  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
   const WorkspaceLayout w = use_balanced(q_dtype, num_seqs, partition_tokens)
                                 ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim)
@@ -317,9 +323,10 @@ PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
   if (!valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_kv_heads > 256) return PA_ERR_BAD_SHAPE;   // scales are copied by one workgroup's lanes
+  if (cache_dtype == PA_DTYPE_INT4 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL_POINTER;
-  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
   CopyBlocksArgs a{k_cache, v_cache, k_scale, v_scale, block_pairs, num_pairs, num_kv_heads, head_dim,
                    num_blocks, cache_dtype};
@@ -343,6 +350,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
   if (q_dtype != PA_DTYPE_BF16 || cache_dtype == PA_DTYPE_F32) return PA_ERR_BAD_DTYPE;
+  if (cache_dtype == PA_DTYPE_INT4 && in.head_dim != 128) return PA_ERR_UNSUPPORTED;
   const PlanLayout lay = plan_layout(in);
   if ((int64_t)lay.bytes != in.plan_bytes) return PA_ERR_BAD_SHAPE;
   if ((int64_t)planned_workspace_bytes(in) != in.workspace_bytes) return PA_ERR_BAD_SHAPE;
@@ -350,7 +358,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   if (in.num_columns < 1 || in.num_wgs < 1) return PA_ERR_BAD_SHAPE;
   if (in.num_merge_rows > 0 && (in.num_records < 1 || in.num_merge_entries < 1)) return PA_ERR_BAD_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !plan) return PA_ERR_NULL_POINTER;
-  if (cache_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
+  if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(plan))
     return PA_ERR_MISALIGNED;
   const size_t ws_need = planned_workspace_bytes(in);

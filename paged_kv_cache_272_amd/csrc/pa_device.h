@@ -5,6 +5,7 @@
 //    narrowing rounds to nearest even.
 //  * e4m3 is the OCP "E4M3FN" 8-bit float: sign, 4 exponent bits (bias 7),
 //    3 mantissa bits, subnormals m * 2^-9, NaN = S.1111.111, max 448.
+//  * int4 is a signed integer in [-8, 7] stored as the 4-bit code value + 8.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,6 +62,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat_rne(float x) {
   uint32_t ri = (uint32_t)r;
   if (ri == 16u) { ri = 8u; E += 1; }
   return sign | ((uint32_t)(E + 7) << 3) | (ri - 8u);
+}
+
+// int4 code of a binary32 value: round half to even (the default rounding
+// of rint), clamp to [-8, 7], offset by 8.  NaN gives code 0.
+__device__ __forceinline__ uint32_t f32_to_int4_code(float x) {
+  const float r = fminf(fmaxf(__builtin_rintf(x), -8.0f), 7.0f);
+  return (uint32_t)(int)(r + 8.0f);
 }
 
 // --- wave-level reductions (64 lanes) ---------------------------------------

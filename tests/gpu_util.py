@@ -11,7 +11,7 @@ import torch
 import oracle
 import pa_workloads as W
 
-TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2, "int4": 1e-2}
 
 
 def log(msg: str) -> None:
@@ -40,10 +40,10 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def quantize_fp8_values(wl: W.PagedWorkload) -> None:
-    """Turn an fp8 'values' workload into codes with the oracle's quantiser (CPU)."""
+    """Turn an fp8 or int4 'values' workload into codes with the oracle's quantiser (CPU)."""
     if wl.k_cache is None:
-        wl.k_cache = oracle.quantize_pool_ref(wl.k_values, wl.k_scale)
-        wl.v_cache = oracle.quantize_pool_ref(wl.v_values, wl.v_scale)
+        wl.k_cache = oracle.quantize_pool_ref(wl.k_values, wl.k_scale, wl.kv_dtype)
+        wl.v_cache = oracle.quantize_pool_ref(wl.v_values, wl.v_scale, wl.kv_dtype)
 
 
 class DeviceWorkload:

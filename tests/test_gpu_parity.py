@@ -115,13 +115,12 @@ def _append_parity(wl, partition_tokens=None):
     assert err <= TOL[wl.kv_dtype]
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
 def test_decode_append_fused(kv):
     lens = [1, 15, 16, 17, 33, 700, 1500, 4096, 2049, 5]
     wl = W.make_workload(name="append", seed=109, context_lens=lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
                          q_dtype="bf16", kv_dtype=kv, fp8_mode="values")
-    if kv == "fp8":
-        quantize_fp8_values(wl)
+    quantize_fp8_values(wl)
     _append_parity(wl)
 
 
@@ -133,14 +132,13 @@ def test_decode_append_many_short_sequences():
     _append_parity(wl)
 
 
-@pytest.mark.parametrize("kv,p", [("f32", 0), ("bf16", 256), ("fp8", 512)])
+@pytest.mark.parametrize("kv,p", [("f32", 0), ("bf16", 256), ("fp8", 512), ("int4", 256)])
 def test_decode_append_unfused_paths(kv, p):
     qd = "f32" if kv == "f32" else "bf16"
     wl = W.make_workload(name="append_unfused", seed=112, context_lens=[3, 16, 17, 600, 1100], num_q_heads=8,
                          num_kv_heads=4, head_dim=128, q_dtype=qd, kv_dtype=kv, fp8_mode="values",
                          sigma=1.0 if kv == "f32" else 0.5)
-    if kv == "fp8":
-        quantize_fp8_values(wl)
+    quantize_fp8_values(wl)
     _append_parity(wl, partition_tokens=p)
 
 
@@ -156,23 +154,22 @@ EDGE_CTX = [1, 15, 16, 17, 512, 513]
 
 @pytest.mark.parametrize("hq,hkv,d,kv", [(4, 4, 64, "f32"), (8, 2, 128, "f32"), (16, 1, 64, "bf16"),
                                          (32, 8, 128, "bf16"), (64, 8, 128, "bf16"), (16, 16, 128, "bf16"),
-                                         (64, 8, 128, "fp8"), (8, 8, 64, "fp8")])
+                                         (64, 8, 128, "fp8"), (8, 8, 64, "fp8"), (32, 8, 128, "int4"),
+                                         (16, 1, 128, "int4")])
 def test_boundary_lengths_and_groups(hq, hkv, d, kv):
     qd = "f32" if kv == "f32" else "bf16"
     wl = W.make_workload(name="edge", seed=101, context_lens=EDGE_CTX, num_q_heads=hq, num_kv_heads=hkv,
                          head_dim=d, q_dtype=qd, kv_dtype=kv, fp8_mode="values",
                          sigma=1.0 if kv == "f32" else 0.5)
-    if kv == "fp8":
-        quantize_fp8_values(wl)
+    quantize_fp8_values(wl)
     _full_parity(wl, len(EDGE_CTX), True)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
 def test_partition_size_invariance(kv):
     wl = W.make_workload(name="parts", seed=102, context_lens=[700, 33, 1500, 16, 1], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv, fp8_mode="values")
-    if kv == "fp8":
-        quantize_fp8_values(wl)
+    quantize_fp8_values(wl)
     dw = DeviceWorkload(wl)
     k_ref, v_ref = oracle_after_write(wl)
     dw.cache_write(pa)
@@ -196,8 +193,7 @@ def test_many_short_sequences(hq, hkv, d, kv):
     lens[::37] = rng.integers(300, 900, size=len(lens[::37]))
     wl = W.make_workload(name="short", seed=106, context_lens=lens, num_q_heads=hq, num_kv_heads=hkv,
                          head_dim=d, q_dtype="bf16", kv_dtype=kv, fp8_mode="values")
-    if kv == "fp8":
-        quantize_fp8_values(wl)
+    quantize_fp8_values(wl)
     _full_parity(wl, 40, False)
 
 
@@ -262,6 +258,17 @@ def test_workspace_reused_across_calls():
                      dw.context_lens[:2].contiguous(), wl.max_context_len, wl.scale, workspace=ws)
         torch.cuda.synchronize()
         assert np.abs(out_to_f64(sub) - want[:2]).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["values", "codes"])
+def test_int4_8b_shape(mode):
+    """The 8B-shaped batch (64 sequences, contexts 128..4096) with an int4 KV cache."""
+    base = W.config2(with_values=False)
+    wl = W.make_workload(name="int4-8b", seed=110, context_lens=[int(c) for c in base.context_lens],
+                         num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="int4",
+                         fp8_mode=mode)
+    quantize_fp8_values(wl)
+    _full_parity(wl, 12, False)
 
 
 def test_stale_workspace_and_fewer_units_than_slices():

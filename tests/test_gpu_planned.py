@@ -39,7 +39,8 @@ def _multi_query_case(name, seed, ctxs, q_lens, hq, hkv, d, kv, fp8_mode="values
 
 
 @pytest.mark.parametrize("hq,hkv,d,kv", [(32, 8, 128, "bf16"), (64, 8, 128, "bf16"), (8, 8, 64, "bf16"),
-                                         (16, 1, 64, "bf16"), (32, 8, 128, "fp8"), (64, 8, 128, "fp8")])
+                                         (16, 1, 64, "bf16"), (32, 8, 128, "fp8"), (64, 8, 128, "fp8"),
+                                         (32, 8, 128, "int4")])
 def test_multi_query_parity(hq, hkv, d, kv):
     ctxs = [40, 7, 100, 16, 33, 300, 1, 520]
     q_lens = [5, 7, 0, 16, 1, 37, 1, 4]
