@@ -29,7 +29,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f32, e4m3_quantize, int4_quantize
+from .formats import bf16_to_f32, e4m3_quantize, e4m3_to_f64, int4_quantize, int4_to_f64
 
 BLOCK = 16
 
@@ -101,3 +101,64 @@ def copy_blocks_ref(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray,
             ks[dst] = ks[src]
             vs[dst] = vs[src]
     return k_out, v_out, ks, vs
+
+
+def _decode_codes(codes: np.ndarray, cache_dtype: str) -> np.ndarray:
+    """float32 value of stored codes (e4m3 bytes, or packed int4 unpacked along the last axis)."""
+    if cache_dtype == "fp8":
+        return e4m3_to_f64(codes).astype(np.float32)
+    return int4_to_f64(codes).astype(np.float32)
+
+
+def cache_write_autoscale_ref(k_cache: np.ndarray, v_cache: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                              new_k: np.ndarray, new_v: np.ndarray, slot_mapping: np.ndarray, src_dtype: str,
+                              cache_dtype: str):
+    """Slot scatter into an e4m3 or int4 cache that sets the block scales itself.
+
+    The rows one call writes into a block form a run (consecutive tokens of the
+    call, consecutive offsets from o0).  Per (block, head), with top = 448
+    (e4m3) or 7 (int4) and a = max |x| over the run's new values:
+      * o0 == 0 (the block starts here): scale = a / top (1 if a == 0);
+      * otherwise, if a > old_scale * top, the scale grows to a / top and the
+        rows already in the block (offsets < o0) are re-encoded: value =
+        float32(code value) * old_scale, code = encode(value / new_scale);
+      * otherwise the old scale stays.
+    The new rows are then encoded with the block's scale, as cache_write_ref
+    does.  All arithmetic is float32 (IEEE products and quotients).
+    Returns (k_cache, v_cache, k_scale, v_scale), new arrays.
+    """
+    top = np.float32(448.0 if cache_dtype == "fp8" else 7.0)
+    quantize = e4m3_quantize if cache_dtype == "fp8" else int4_quantize
+    outs = []
+    for cache, scale, new in ((k_cache, k_scale, new_k), (v_cache, v_scale, new_v)):
+        cache = np.array(cache, copy=True)
+        scale = np.array(scale, dtype=np.float32, copy=True)
+        slots = np.asarray(slot_mapping, dtype=np.int64)
+        t = 0
+        while t < len(slots):
+            if slots[t] < 0:
+                t += 1
+                continue
+            blk, o0 = int(slots[t]) // BLOCK, int(slots[t]) % BLOCK
+            e = t + 1
+            while e < len(slots) and slots[e] >= 0 and int(slots[e]) // BLOCK == blk:
+                e += 1
+            rows = _src_f32(new[t:e], src_dtype)                            # [n, Hkv, D]
+            for h in range(cache.shape[1]):
+                a = np.float32(np.abs(rows[:, h, :]).max())
+                old = scale[blk, h]
+                if o0 == 0:
+                    s = np.float32(a / top) if a > 0 else np.float32(1.0)
+                elif a > np.float32(old * top):
+                    s = np.float32(a / top)
+                    kept = _decode_codes(cache[blk, h, :o0], cache_dtype) * old   # float32 products
+                    cache[blk, h, :o0] = quantize(kept, s)
+                else:
+                    s = old
+                scale[blk, h] = s
+                for i in range(e - t):
+                    off = int(slots[t + i]) % BLOCK
+                    cache[blk, h, off] = quantize(rows[i, h], s)
+            t = e
+        outs.append((cache, scale))
+    return outs[0][0], outs[1][0], outs[0][1], outs[1][1]
