@@ -106,6 +106,33 @@ int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype,
                    void* stream);
 
 /*
+ * pa_cache_write_autoscale — slot scatter into an e4m3 or int4 cache that
+ * sets the per-(block, head) scales itself (k_scale/v_scale are read and
+ * written).
+ *
+ * The rows one call writes into one block must be consecutive tokens of the
+ * call with consecutive offsets (a prefill chunk, or one decode token per
+ * sequence); such a run starting at offset o0 is handled per KV head with
+ * a = max |x| over its values and top = 448 (e4m3) or 7 (int4):
+ *   - o0 == 0 (the run starts the block): scale = a / top (1 if a == 0);
+ *   - else if a > scale * top: the scale grows to a / top and the rows
+ *     already in the block are re-encoded (code value * old scale, divided
+ *     by the new scale, encoded again);
+ *   - else the scale stays.
+ * The new rows are then encoded with the block's scale as pa_cache_write
+ * does.  So no value is clipped, and the scales need no calibration pass
+ * ("推理优化" section 五 exercise 1 and "17 · 连续批处理与 PagedAttention"
+ * section 四 name fp8/int4 KV caches; how their scales are chosen is this
+ * library's reading).  src_dtype F32 or BF16.  Errors as pa_cache_write.
+ */
+int pa_cache_write_autoscale(const void* k, const void* v, pa_dtype src_dtype,
+                             void* k_cache, void* v_cache, pa_dtype cache_dtype,
+                             float* k_scale, float* v_scale,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                             void* stream);
+
+/*
  * pa_decode_partition_tokens — the partition length pa_decode uses.
  *
  * Returns `partition_tokens` itself when it is positive, otherwise the

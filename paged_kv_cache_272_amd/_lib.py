@@ -62,6 +62,8 @@ class PlanInfo(ctypes.Structure):
 _SIGNATURES = {
     "pa_cache_write": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                       _i32, _i32, _i32, _i32, _vp]),
+    "pa_cache_write_autoscale": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                                _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32,
@@ -159,6 +161,23 @@ def pa_cache_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_ca
     _check(_lib.pa_cache_write(_ptr(k), _ptr(v), dtype_code(k), _ptr(k_cache), _ptr(v_cache),
                                cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
                                k.shape[0], hkv, d, num_blocks, _stream(stream)), "pa_cache_write")
+
+
+def pa_cache_write_autoscale(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             k_scale: torch.Tensor, v_scale: torch.Tensor, slot_mapping: torch.Tensor,
+                             stream=None) -> None:
+    """Slot scatter into an e4m3 or int4 cache (uint8 pools; int4 rows hold D/2
+    bytes) that sets the (block, head) scales itself: k_scale/v_scale
+    [NB, Hkv] float32 are read and written."""
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    num_blocks, hkv, bs, _ = k_cache.shape
+    d = k.shape[-1]
+    if bs != BLOCK_SIZE or tuple(k.shape) != (k.shape[0], hkv, _row(k_cache, d)) or k.shape != v.shape:
+        raise ValueError("shape mismatch between new K/V and the cache")
+    _check(_lib.pa_cache_write_autoscale(_ptr(k), _ptr(v), dtype_code(k), _ptr(k_cache), _ptr(v_cache),
+                                         cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
+                                         k.shape[0], hkv, d, num_blocks, _stream(stream)), "pa_cache_write_autoscale")
 
 
 def pa_decode_partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

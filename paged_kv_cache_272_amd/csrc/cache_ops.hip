@@ -128,6 +128,100 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_int4_kernel(CacheWr
   }
 }
 
+// ---- slot scatter that sets the (block, head) scales itself
+//
+// The rows a call writes into one block are consecutive tokens of the call
+// (a "run"); the workgroup of the run's first token handles the whole run,
+// head by head: a = max |x| over the run's values; a block started by the
+// run takes scale a / top, an append whose values exceed old_scale * top
+// grows the scale and re-encodes the rows already in the block
+// (value = code value * old scale, code = encode(value / new scale)), and
+// the new rows are encoded with the final scale.  top = 448 (e4m3) or 7
+// (int4).  All arithmetic is binary32, products and quotients rounded once.
+constexpr int kScaleThreads = 256;
+
+template <bool kInt4, bool kSrcBf16>
+__global__ __launch_bounds__(kScaleThreads) void cache_write_autoscale_kernel(CacheWriteArgs a, float* k_scale,
+                                                                              float* v_scale) {
+  __shared__ float s_red[kScaleThreads / 64];
+  const int t0 = blockIdx.x;
+  const bool is_v = blockIdx.y != 0;
+  const int64_t slot0 = a.slot_mapping[t0];
+  const int64_t pool = (int64_t)a.num_blocks * kBlockTokens;
+  if (slot0 < 0 || slot0 >= pool) return;
+  const int64_t blk = slot0 / kBlockTokens;
+  if (t0 > 0) {
+    const int64_t prev = a.slot_mapping[t0 - 1];
+    if (prev >= 0 && prev < pool && prev / kBlockTokens == blk) return;      // not the run's first token
+  }
+  int n = 1;                                                                // run length (<= 16)
+  while (n < kBlockTokens && t0 + n < a.num_tokens) {
+    const int64_t s = a.slot_mapping[t0 + n];
+    if (s < 0 || s >= pool || s / kBlockTokens != blk) break;
+    ++n;
+  }
+  const int o0 = (int)(slot0 % kBlockTokens);
+  const int D = a.head_dim;
+  const int row_bytes = kInt4 ? D / 2 : D;
+  const float top = kInt4 ? 7.0f : 448.0f;
+  float* scales = is_v ? v_scale : k_scale;
+  uint8_t* cache = reinterpret_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(is_v ? a.v : a.k);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto load = [&](int i, int h, int d) -> float {     // value d of head h of the run's row i
+    const int64_t e = ((int64_t)(t0 + i) * a.num_kv_heads + h) * D + d;
+    if constexpr (kSrcBf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[e]);
+    else return reinterpret_cast<const float*>(src)[e];
+  };
+  auto encode = [&](float x) -> uint32_t {
+    if constexpr (kInt4) return f32_to_int4_code(x);
+    else return f32_to_e4m3_sat_rne(x);
+  };
+  for (int h = 0; h < a.num_kv_heads; ++h) {
+    // a = max |x| over the run's new values of this head
+    float amax = 0.0f;
+    for (int i = tid; i < n * D; i += kScaleThreads) amax = fmaxf(amax, fabsf(load(i / D, h, i % D)));
+    amax = wave_max(amax);
+    if (lane == 0) s_red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    const float old = scales[blk * a.num_kv_heads + h];
+    float s = old;
+    bool grow = false;
+    if (o0 == 0) {
+      s = amax > 0.0f ? __fdiv_rn(amax, top) : 1.0f;
+    } else if (amax > old * top) {
+      s = __fdiv_rn(amax, top);
+      grow = true;
+    }
+    uint8_t* head_rows = cache + ((blk * a.num_kv_heads + h) * kBlockTokens) * row_bytes;
+    if (grow) {                                         // re-encode the rows already in the block
+      for (int i = tid; i < o0 * row_bytes; i += kScaleThreads) {
+        const uint32_t b = head_rows[i];
+        uint32_t out;
+        if constexpr (kInt4) {
+          const float lo = (float)((int)(b & 15u) - 8) * old, hi = (float)((int)(b >> 4) - 8) * old;
+          out = encode(__fdiv_rn(lo, s)) | (encode(__fdiv_rn(hi, s)) << 4);
+        } else {
+          out = encode(__fdiv_rn(e4m3_to_f32(b) * old, s));
+        }
+        head_rows[i] = (uint8_t)out;
+      }
+    }
+    // the new rows with the block's final scale
+    for (int i = tid; i < n * row_bytes; i += kScaleThreads) {
+      const int r = i / row_bytes, j = i % row_bytes;
+      uint32_t out;
+      if constexpr (kInt4) out = encode(__fdiv_rn(load(r, h, 2 * j), s)) | (encode(__fdiv_rn(load(r, h, 2 * j + 1), s)) << 4);
+      else out = encode(__fdiv_rn(load(r, h, j), s));
+      head_rows[(int64_t)(o0 + r) * row_bytes + j] = (uint8_t)out;
+    }
+    if (tid == 0) scales[blk * a.num_kv_heads + h] = s;
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArgs a, int block_chunks) {
   const int i = blockIdx.x;
   const bool is_v = blockIdx.y != 0;
@@ -159,6 +253,24 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
   } else {
     const int e = a.cache_dtype == PA_DTYPE_F32 ? 4 : 2;
     hipLaunchKernelGGL(cache_write_copy_kernel, grid, dim3(kWriteThreads), 0, stream, a, e);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write_autoscale(const CacheWriteArgs& a, float* k_scale, float* v_scale,
+                                       hipStream_t stream) {
+  const dim3 grid(a.num_tokens, 2);
+  const bool int4 = a.cache_dtype == PA_DTYPE_INT4, bf16 = a.src_dtype == PA_DTYPE_BF16;
+  if (int4) {
+    if (bf16) hipLaunchKernelGGL((cache_write_autoscale_kernel<true, true>), grid, dim3(kScaleThreads), 0, stream, a,
+                                 k_scale, v_scale);
+    else hipLaunchKernelGGL((cache_write_autoscale_kernel<true, false>), grid, dim3(kScaleThreads), 0, stream, a,
+                            k_scale, v_scale);
+  } else {
+    if (bf16) hipLaunchKernelGGL((cache_write_autoscale_kernel<false, true>), grid, dim3(kScaleThreads), 0, stream,
+                                 a, k_scale, v_scale);
+    else hipLaunchKernelGGL((cache_write_autoscale_kernel<false, false>), grid, dim3(kScaleThreads), 0, stream, a,
+                            k_scale, v_scale);
   }
   return hipGetLastError();
 }

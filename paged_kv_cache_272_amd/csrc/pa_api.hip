@@ -174,6 +174,24 @@ PA_EXPORT int pa_cache_write(const void* k, const void* v, pa_dtype src_dtype, v
   return launch_cache_write(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+PA_EXPORT int pa_cache_write_autoscale(const void* k, const void* v, pa_dtype src_dtype, void* k_cache,
+                                       void* v_cache, pa_dtype cache_dtype, float* k_scale, float* v_scale,
+                                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_BAD_SHAPE;
+  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  if (!scaled_dtype(cache_dtype)) return PA_ERR_BAD_DTYPE;
+  if (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_BF16) return PA_ERR_BAD_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (cache_dtype == PA_DTYPE_INT4 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale) return PA_ERR_NULL_POINTER;
+  CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, nullptr, nullptr, num_tokens,
+                   num_kv_heads, head_dim, num_blocks, 0, src_dtype, cache_dtype};
+  return launch_cache_write_autoscale(a, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK : PA_ERR_LAUNCH;
+}
+
 PA_EXPORT int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t max_context_len,
                                              int32_t partition_tokens) {

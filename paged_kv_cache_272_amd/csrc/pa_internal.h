@@ -83,6 +83,9 @@ struct DecodeArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+// Slot scatter into an e4m3/int4 cache that sets the (block, head) scales.
+hipError_t launch_cache_write_autoscale(const CacheWriteArgs& a, float* k_scale, float* v_scale,
+                                       hipStream_t stream);
 
 // Partition kernels (partition grid): writes `out` directly for sequences
 // that fit one partition, partial results into the workspace otherwise.
