@@ -342,7 +342,8 @@ def prepare_attend_planned(out, q, k_cache, v_cache, block_tables, scale, plan, 
         workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), cache_code(k_cache, info.head_dim),
-            _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], num_blocks, float(scale), _ptr(plan),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], num_blocks, float(scale),
+            _ptr(plan),
             ctypes.byref(info), _ptr(workspace), ws_bytes, _stream(stream))
     return PreparedCall("pa_attend_planned", args, (out, q, k_cache, v_cache, block_tables, k_scale, v_scale,
                                                     plan, info, workspace))

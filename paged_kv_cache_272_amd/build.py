@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["pa_api.hip", "plan.cpp", "block_manager.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip", "attend_planned.hip",
-           "probes.hip"]
+SOURCES = ["pa_api.hip", "plan.cpp", "block_manager.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
+           "attend_planned.hip", "probes.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

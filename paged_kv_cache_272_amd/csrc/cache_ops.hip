@@ -213,7 +213,8 @@ __global__ __launch_bounds__(kScaleThreads) void cache_write_autoscale_kernel(Ca
     for (int i = tid; i < n * row_bytes; i += kScaleThreads) {
       const int r = i / row_bytes, j = i % row_bytes;
       uint32_t out;
-      if constexpr (kInt4) out = encode(__fdiv_rn(load(r, h, 2 * j), s)) | (encode(__fdiv_rn(load(r, h, 2 * j + 1), s)) << 4);
+      if constexpr (kInt4)
+        out = encode(__fdiv_rn(load(r, h, 2 * j), s)) | (encode(__fdiv_rn(load(r, h, 2 * j + 1), s)) << 4);
       else out = encode(__fdiv_rn(load(r, h, j), s));
       head_rows[(int64_t)(o0 + r) * row_bytes + j] = (uint8_t)out;
     }

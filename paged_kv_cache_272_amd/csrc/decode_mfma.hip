@@ -399,8 +399,8 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
 // w_first..w_last; its partial sits in slot 1 of w_first (it began inside
 // that slice) and in slot 0 of every later one.
 //   out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w,
-// taken in one pass with a running maximum, four partials per round so their
-// loads are in flight together.  Grid (sequence, chunk group): each thread
+// taken in one pass with a running maximum, eight partials per round so
+// their loads are in flight together.  Grid (sequence, chunk group): each thread
 // owns one 4-wide chunk of one query head's output row.
 constexpr int kMergeThreads = 256;
 
@@ -420,11 +420,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_balanced_kernel(De
   const int h = it / kChunks, ch = it % kChunks;
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int w0 = 0; w0 < n; w0 += 4) {
-    float mv[4], lv[4];
-    float4 av[4];
+  constexpr int kBatch = 8;                            // partial rows whose loads are in flight together
+  for (int w0 = 0; w0 < n; w0 += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    float4 av[kBatch];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const int w = wf + w0 + k;
       if (w0 + k < n) {
         const int64_t row = ((int64_t)w * 2 + (w == wf ? 1 : 0)) * a.num_q_heads + h;
@@ -437,12 +438,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_balanced_kernel(De
         av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
-    const float Mn = fmaxf(M, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) Mn = fmaxf(Mn, mv[k]);
     const float sc = __builtin_amdgcn_exp2f(M - Mn);          // 0 while M is still -inf
     den *= sc;
     num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const float wt = __builtin_amdgcn_exp2f(mv[k] - Mn);    // 0 for the padding entries
       den += wt * lv[k];
       num.x += wt * av[k].x; num.y += wt * av[k].y; num.z += wt * av[k].z; num.w += wt * av[k].w;

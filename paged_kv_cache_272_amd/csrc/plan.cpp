@@ -3,8 +3,9 @@
 //
 // A query column is one (new token, query head within its GQA group) pair;
 // it becomes one N-column of an MFMA tile.  A wave holds up to two tiles of
-// 16 columns, so up to 32 columns share every K/V block the wave loads.  New token i of a sequence with q_len new tokens
-// and context ctx sits at position ctx - q_len + i and sees positions
+// 16 columns, so up to 32 columns share every K/V block the wave loads.
+// New token i of a sequence with q_len new tokens and context ctx sits at
+// position ctx - q_len + i and sees positions
 // 0 .. ctx - q_len + i (the causal mask of "系统级优化…" section 3.3,
 // aligned to the end of the context; the multi-token steps are chunked
 // prefill, "17 · 连续批处理与 PagedAttention" section 二, and speculative

@@ -69,7 +69,8 @@ def test_driver_matches_oracle_shadow():
                 break
             except oracle.block_manager_ref.OutOfBlocks:
                 with pytest.raises(pa.OutOfBlocks):
-                    drv.step(running, _dev(q[:b]), _dev(kn[:b]), _dev(vn[:b]), torch.empty(b, HQ, D, dtype=torch.bfloat16, device="cuda"))
+                    drv.step(running, _dev(q[:b]), _dev(kn[:b]), _dev(vn[:b]),
+                             torch.empty(b, HQ, D, dtype=torch.bfloat16, device="cuda"))
                 victim = running.pop()
                 ref.free_seq(victim)
                 drv.finish(victim)
