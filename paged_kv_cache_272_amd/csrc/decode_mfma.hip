@@ -167,9 +167,24 @@ __device__ __forceinline__ int slice_of(int u, int U, int n) {
   return (int)(((int64_t)(u + 1) * n + U - 1) / U) - 1;
 }
 
+// Finished rows are staged through LDS kStageRows at a time (a group of up
+// to 16 query heads takes two passes); the stage follows start[] and ctx[]
+// in the dynamic LDS, 16-byte aligned.  LDS per workgroup:
+// 4*(2B+1) + 8 waves * 8 rows * D * 4 bytes <= 32 KB + 32 KB for B <= 4096.
+constexpr int kStageRows = 8;
+__host__ __device__ constexpr int balanced_stage_offset_words(int num_seqs) { return (2 * num_seqs + 1 + 3) / 4 * 4; }
+
+// Make this wave's LDS writes visible to its other lanes' later LDS reads
+// (and finish its reads before later writes): wait for the wave's LDS
+// operations, and keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_wave_barrier();
+}
+
 struct UnitIds {
-  int b, i, blk;       // lane j: the (sequence, logical block, physical block) of unit base + j
-  float ks, vs;        // fp8 block scales of that unit for this wave's head
+  int b, i, blk;       // lane j: the (sequence, logical block, raw table entry) of unit base + j
 };
 
 __device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int u) {
@@ -183,38 +198,70 @@ __device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int
   return lo;
 }
 
-template <bool kScaled>
-__device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int g,
-                                            int lane) {
-  UnitIds id{0, 0, 0, 1.0f, 1.0f};
+// Table entries of 64 units, one per lane, waited for here: a register
+// holding a load still in flight cannot be copied without a wait, and the
+// compiler copies these ids across loop iterations.  One wait per 64 units.
+__device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int lane) {
+  UnitIds id{0, 0, 0};
   const int u = base + lane;
   if (u < u1) {
     id.b = find_sequence(start, a.num_seqs, u);
     id.i = u - start[id.b];
-    id.blk = clamp_block(a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i], a.num_blocks);
-    if constexpr (kScaled) {
-      id.ks = a.k_scale[(int64_t)id.blk * a.num_kv_heads + g];
-      id.vs = a.v_scale[(int64_t)id.blk * a.num_kv_heads + g];
-    }
+    id.blk = a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i];
   }
+  asm volatile("" : "+v"(id.blk));
   return id;
 }
 
 template <int D, int kFmt>
 struct Pending {
   BlockRegs<D, kFmt> regs;
+  uint4 q[D / 32];          // query rows of the unit's sequence (load_query), used when the unit starts it
   int64_t blk;
-  int b, i;
+  int b, i, ctx;
   float ks, vs;
+  bool live;                // false: a fetch past the slice's end (a copy of its last unit, folded in as a no-op)
+  bool starts;              // first unit of its sequence in this slice
   int off;                  // appending: slot of the sequence's newest token in this block, else -1
-  uint32_t nk[D / 8];       // its K run (lane r == off) as bf16 pairs
-  uint32_t nv[D / 32];      // its V run (lane group c == off / 4) as bf16 pairs
+  bool row_staged;          // ... and that token's K/V runs sit in the staging registers
 };
+
+// e4m3/int4 caches: registers for the newest token's bf16 runs, filled in
+// fetch() when a unit holds that token.  One set serves both units in
+// flight: when the other unit still holds it (two sequences ending one unit
+// apart) the unit loads at consume time instead and waits there.
+template <int D>
+struct Staging {
+  uint32_t nk[D / 8];       // K run (lane r == off) as bf16 pairs
+  uint32_t nv[D / 32];      // V run (lane group c == off / 4)
+  bool row_busy = false;
+};
+
+// bf16 cache: a block's registers, where the lanes that hold the newest
+// token's K run (r == off) and V run (token 4c+e == off) read it from the new
+// rows kn, vn instead of the cache slot (written later in the same launch).
+// off = -1: a plain block load.
+template <int D>
+__device__ __forceinline__ void load_block_with_row(BlockRegs<D, kFmtBf16>& br, const uint8_t* kbase,
+                                                    const uint8_t* vbase, int64_t blk, int num_kv_heads, int g, int r,
+                                                    int c, int off, const uint16_t* kn, const uint16_t* vn) {
+  using T = Tile<D, kFmtBf16>;
+  const int64_t head_base = (blk * num_kv_heads + g) * kBlockTokens;
+  const uint8_t* kp = r == off ? reinterpret_cast<const uint8_t*>(kn + (D / 4) * c)
+                               : kbase + T::bytes((head_base + r) * D + (D / 4) * c);
+  load_words<T::kKWords>(kp, br.k);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint8_t* vp = 4 * c + e == off ? reinterpret_cast<const uint8_t*>(vn + T::kE * r)
+                                         : vbase + T::bytes((head_base + 4 * c + e) * D + T::kE * r);
+    load_words<T::kVWords>(vp, br.v[e]);
+  }
+}
 
 template <int D, int kFmt>
 __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_kernel(DecodeArgs a) {
   constexpr int kE = Tile<D, kFmt>::kE;
-  extern __shared__ int s_dyn[];                 // start[B + 1], then ctx[B]
+  extern __shared__ int s_dyn[];                 // start[B + 1], ctx[B], then per wave kStageRows x D floats
   __shared__ int s_wave_tot[kBalancedMaxWaves];
   int* s_start = s_dyn;
   int* s_ctx = s_dyn + a.num_seqs + 1;
@@ -280,117 +327,173 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
 
   HeadState<D, kFmt> hs;
   int cur_b = -1;
+  // The G rows a wave finishes are consecutive in `out` and in the
+  // workspace, but each lane holds a 16-byte-strided run of one row; stores
+  // straight from those registers would split every cache line over many
+  // requests.  The rows go through this wave's LDS stage instead and leave
+  // as whole 16-byte pieces, consecutive lanes writing consecutive pieces.
+  float* stage = reinterpret_cast<float*>(s_dyn + balanced_stage_offset_words(a.num_seqs)) + wave * kStageRows * D;
   auto finish = [&](int b) {
     const float L = hs.total_l();
     float o[4 * kE];
     hs.unpack(o);
-    if (r >= G) return;
-    const int64_t row = (int64_t)b * a.num_q_heads + (int64_t)g * G + r;
+    const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;   // rows row0 .. row0+G-1
     const bool whole = s_start[b] >= u0 && s_start[b + 1] <= u1;
-    if (whole) {
-      store_bf16_run<D>(out + row * D, d0, o, 1.0f / L);
-    } else {
-      const int slot = s_start[b] < u0 ? 0 : 1;
-      const int64_t wr = ((int64_t)x * 2 + slot) * a.num_q_heads + (int64_t)g * G + r;
-      store_f32_run<D>(a.ws_acc + wr * D, d0, o);
-      if (c == 0) {
-        a.ws_m[wr] = hs.m;
-        a.ws_l[wr] = L;
+    const int slot = s_start[b] < u0 ? 0 : 1;
+    const int64_t wr0 = ((int64_t)x * 2 + slot) * a.num_q_heads + (int64_t)g * G;
+    if (!whole && c == 0 && r < G) {
+      a.ws_m[wr0 + r] = hs.m;
+      a.ws_l[wr0 + r] = L;
+    }
+    for (int rr = 0; rr < G; rr += kStageRows) {
+      const int nr = min(kStageRows, G - rr);
+      const bool mine = r >= rr && r < rr + nr;
+      wave_lds_sync();                       // the previous pass's reads are done
+      if (whole) {
+        if (mine) store_bf16_run<D>(reinterpret_cast<uint16_t*>(stage) + (r - rr) * D, d0, o, 1.0f / L);
+        wave_lds_sync();
+        const uint4* src = reinterpret_cast<const uint4*>(stage);
+        uint4* dst = reinterpret_cast<uint4*>(out + (row0 + rr) * D);
+        for (int pc = lane; pc < nr * D / 8; pc += 64) dst[pc] = src[pc];
+      } else {
+        if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
+        wave_lds_sync();
+        const float4* src = reinterpret_cast<const float4*>(stage);
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (wr0 + rr) * D);
+        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = src[pc];
       }
     }
   };
 
-  // ids of the current 64-unit chunk and of the next one (kept one chunk ahead)
+  // Table entries of the current 64-unit chunk.
   int base = u0;
-  UnitIds cur = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base, u1, g, lane);
-  UnitIds nxt = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base + 64, u1, g, lane);
+  UnitIds cur = unit_ids(a, s_start, base, u1, lane);
+
+  // Vector memory operations complete in issue order and are waited for by
+  // a count the compiler fixes per program point, taking the path with the
+  // fewest operations issued after the awaited one.  So everything a unit
+  // needs is loaded in fetch() (a load issued at consume time, after the
+  // other unit's block, would make this wait for that block), and fetch()
+  // issues the same loads on every path: the query rows of the unit's
+  // sequence come with every unit (cache hits after its first), not only
+  // with the unit that starts the sequence.  Only the e4m3/int4 new-token
+  // runs are conditional (once per sequence).
+  constexpr bool kScaled = kFmt != kFmtBf16;
+  Staging<D> st;
+  int fetched_b = -1;
+  auto q_row = [&](int b) { return (int64_t)b * a.num_q_heads + (int64_t)g * G; };
+  auto new_k = [&](int b) { return reinterpret_cast<const uint16_t*>(a.k_new) + ((int64_t)b * a.num_kv_heads + g) * D; };
+  auto new_v = [&](int b) { return reinterpret_cast<const uint16_t*>(a.v_new) + ((int64_t)b * a.num_kv_heads + g) * D; };
+  // e4m3/int4: the newest token's runs as the splice quantizes them (lane
+  // r == off: K elements d0 .. d0+D/4-1; lane group off/4: V elements (D/16)*r ..)
+  auto load_new_runs = [&](int b, uint32_t* nk, uint32_t* nv) {
+    load_words<D / 8>(reinterpret_cast<const uint8_t*>(new_k(b) + d0), nk);
+    load_words<D / 32>(reinterpret_cast<const uint8_t*>(new_v(b) + (D / 16) * r), nv);
+  };
   auto fetch = [&](Pending<D, kFmt>& p, int u) {
+    p.live = u < u1;
+    u = min(u, u1 - 1);
     if (u - base >= 64) {
       base += 64;
-      cur = nxt;
-      nxt = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base + 64, u1, g, lane);
+      cur = unit_ids(a, s_start, base, u1, lane);
     }
     const int j = u - base;
     p.b = __builtin_amdgcn_readlane(cur.b, j);
     p.i = __builtin_amdgcn_readlane(cur.i, j);
-    p.blk = __builtin_amdgcn_readlane(cur.blk, j);
-    if constexpr (kFmt != kFmtBf16) {
-      p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
-      p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
+    p.blk = clamp_block(__builtin_amdgcn_readlane(cur.blk, j), a.num_blocks);
+    p.ctx = s_ctx[p.b];
+    p.starts = p.b != fetched_b;
+    fetched_b = p.b;
+    load_query<D>(q, q_row(p.b), G, r, c, p.q);
+    // appending: the sequence's last block holds its newest token
+    p.off = p.live && a.append && (p.i + 1) * kBlockTokens >= p.ctx ? (p.ctx - 1) % kBlockTokens : -1;
+    p.row_staged = false;
+    if constexpr (kScaled) {
+      if (p.off >= 0 && !st.row_busy) {
+        st.row_busy = p.row_staged = true;
+        load_new_runs(p.b, st.nk, st.nv);
+      }
+      p.ks = a.k_scale[p.blk * a.num_kv_heads + g];
+      p.vs = a.v_scale[p.blk * a.num_kv_heads + g];
+      load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
     } else {
       p.ks = p.vs = 1.0f;
+      load_block_with_row<D>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c, p.off, new_k(p.b), new_v(p.b));
     }
-    p.off = -1;
-    if (a.append) {
-      const int ctx = s_ctx[p.b];
-      if ((p.i + 1) * kBlockTokens >= ctx) {          // the sequence's last block holds its newest token
-        p.off = (ctx - 1) % kBlockTokens;
-        // every lane loads its runs of the new row; only lane r == off (K) and
-        // lane group off/4 (V) use them
-        const int64_t row = ((int64_t)p.b * a.num_kv_heads + g) * D;
-        load_words<D / 8>(reinterpret_cast<const uint8_t*>(reinterpret_cast<const uint16_t*>(a.k_new) + row + d0),
-                          p.nk);
-        load_words<D / 32>(reinterpret_cast<const uint8_t*>(reinterpret_cast<const uint16_t*>(a.v_new) + row +
-                                                            (D / 16) * r),
-                           p.nv);
-      }
-    }
-    load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
   };
-  // Appending: put the newest token's K/V row into the block this wave holds
-  // and into its slot in the cache (the wave that reads a block is the only
-  // reader of that slot in this launch).
-  auto splice = [&](Pending<D, kFmt>& p) {
+  // Appending: the newest token's K/V row goes into its slot in the cache
+  // (the wave that reads a block is the only reader of that slot in this
+  // launch) and, for e4m3/int4, into the block this wave holds.
+  auto splice = [&](Pending<D, kFmt>& p, const uint32_t* nk, const uint32_t* nv) {
     using T = Tile<D, kFmt>;
     const int64_t head_base = (p.blk * a.num_kv_heads + g) * kBlockTokens;
     uint8_t* kw = const_cast<uint8_t*>(kbase);
     uint8_t* vw = const_cast<uint8_t*>(vbase);
-    if (r == p.off) {
-      uint32_t words[T::kKWords];
-      if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 4>(p.nk, p.ks, words);
-      else if constexpr (kFmt == kFmtInt4) quantize_bf16_words_int4<D / 4>(p.nk, p.ks, words);
-      else
+    if constexpr (!kScaled) {
+      // the registers already hold the new row (load_block_with_row)
+      if (r == p.off) store_words<T::kKWords>(kw + T::bytes((head_base + r) * D + d0), p.regs.k);
 #pragma unroll
-        for (int w = 0; w < T::kKWords; ++w) words[w] = p.nk[w];
+      for (int e = 0; e < 4; ++e)
+        if (4 * c + e == p.off) store_words<T::kVWords>(vw + T::bytes((head_base + p.off) * D + T::kE * r), p.regs.v[e]);
+    } else {
+      if (r == p.off) {
+        uint32_t words[T::kKWords];
+        if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 4>(nk, p.ks, words);
+        else quantize_bf16_words_int4<D / 4>(nk, p.ks, words);
 #pragma unroll
-      for (int w = 0; w < T::kKWords; ++w) p.regs.k[w] = words[w];
-      store_words<T::kKWords>(kw + T::bytes((head_base + r) * D + d0), words);
+        for (int w = 0; w < T::kKWords; ++w) p.regs.k[w] = words[w];
+        store_words<T::kKWords>(kw + T::bytes((head_base + r) * D + d0), words);
+      }
+      uint32_t words[T::kVWords];
+      if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 16>(nv, p.vs, words);
+      else quantize_bf16_words_int4<D / 16>(nv, p.vs, words);
+      // token 4c + ee of this lane's V rows is the new one (by selection: no register indexing)
+#pragma unroll
+      for (int ee = 0; ee < 4; ++ee) {
+        const bool hit = 4 * c + ee == p.off;
+#pragma unroll
+        for (int w = 0; w < T::kVWords; ++w) p.regs.v[ee][w] = hit ? words[w] : p.regs.v[ee][w];
+      }
+      if (c == p.off / 4) store_words<T::kVWords>(vw + T::bytes((head_base + p.off) * D + T::kE * r), words);
     }
-    uint32_t words[T::kVWords];
-    if constexpr (kFmt == kFmtFp8) quantize_bf16_words<D / 16>(p.nv, p.vs, words);
-    else if constexpr (kFmt == kFmtInt4) quantize_bf16_words_int4<D / 16>(p.nv, p.vs, words);
-    else
-#pragma unroll
-      for (int w = 0; w < T::kVWords; ++w) words[w] = p.nv[w];
-    // token 4c + ee of this lane's V rows is the new one (by selection: no register indexing)
-#pragma unroll
-    for (int ee = 0; ee < 4; ++ee) {
-      const bool hit = 4 * c + ee == p.off;
-#pragma unroll
-      for (int w = 0; w < T::kVWords; ++w) p.regs.v[ee][w] = hit ? words[w] : p.regs.v[ee][w];
-    }
-    if (c == p.off / 4) store_words<T::kVWords>(vw + T::bytes((head_base + p.off) * D + T::kE * r), words);
   };
   auto consume = [&](Pending<D, kFmt>& p) {
-    if (p.b != cur_b) {
+    if (p.starts) {
       if (cur_b >= 0) finish(cur_b);
       cur_b = p.b;
-      hs.begin(q, (int64_t)p.b * a.num_q_heads + (int64_t)g * G, G, r, c);
+      hs.begin_loaded(p.q, G, r);
     }
-    if (p.off >= 0) splice(p);
-    const int valid = min(kBlockTokens, s_ctx[p.b] - p.i * kBlockTokens);
+    if (p.off >= 0) {
+      if (!kScaled || p.row_staged) {
+        splice(p, st.nk, st.nv);
+        st.row_busy = false;
+      } else {
+        uint32_t nk[D / 8], nv[D / 32];
+        load_new_runs(p.b, nk, nv);
+#pragma unroll
+        for (int w = 0; w < D / 8; ++w) asm volatile("" : "+v"(nk[w]));
+#pragma unroll
+        for (int w = 0; w < D / 32; ++w) asm volatile("" : "+v"(nv[w]));
+        splice(p, nk, nv);
+      }
+    }
+    // a dead unit repeats one of the sequence's units with no token valid:
+    // the running max, sum and accumulator stay as they are
+    const int valid = p.live ? min(kBlockTokens, p.ctx - p.i * kBlockTokens) : 0;
     hs.step(p.regs, valid, a.scale_log2 * p.ks, p.vs, c);
   };
 
+  // Two units in flight.  The loop body is straight-line (one exit, at the
+  // top; past the slice's end fetch() takes a dead copy of the last unit,
+  // whose lines are cached and whose consume changes nothing), so on every
+  // path the wait before a consume leaves the other unit's loads in flight.
   Pending<D, kFmt> p0, p1;
   fetch(p0, u0);
   for (int u = u0; u < u1; u += 2) {
-    if (u + 1 < u1) fetch(p1, u + 1);
+    fetch(p1, u + 1);
     consume(p0);
-    if (u + 1 < u1) {
-      if (u + 2 < u1) fetch(p0, u + 2);
-      consume(p1);
-    }
+    fetch(p0, u + 2);
+    consume(p1);
   }
   finish(cur_b);
 }
@@ -488,7 +591,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_mfma_balanced(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
-  const size_t lds = (2 * (size_t)a.num_seqs + 1) * sizeof(int);
+  const size_t lds = ((size_t)balanced_stage_offset_words(a.num_seqs) +
+                      (size_t)a.waves_per_wg * kStageRows * a.head_dim) * sizeof(int);
   const int f = kv_format(a.cache_dtype);
 #define PA_LAUNCH(D_, F_) hipLaunchKernelGGL((decode_mfma_balanced_kernel<D_, F_>), grid, block, lds, stream, a)
   if (a.head_dim == 128) {

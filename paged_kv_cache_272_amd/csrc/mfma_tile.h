@@ -189,6 +189,18 @@ __device__ __forceinline__ void load_block(BlockRegs<D, kFmt>& br, const uint8_t
     load_words<T::kVWords>(vbase + T::bytes((head_base + 4 * c + e) * D + T::kE * r), br.v[e]);
 }
 
+// The Q^T operand of HeadState::begin as raw registers: query rows
+// q_row0 .. q_row0+G-1, lane r reading row min(r, G-1), so every lane issues
+// the same loads with no lane-dependent branch (a caller can place them
+// ahead of block loads).  Nothing here uses the loaded words, so they are
+// only waited for where begin_loaded() takes them and zeroes lanes r >= G.
+template <int D>
+__device__ __forceinline__ void load_query(const uint16_t* q, int64_t q_row0, int G, int r, int c, uint4* qw) {
+  const uint16_t* qp = q + (q_row0 + min(r, G - 1)) * D + (D / 4) * c;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) qw[i] = reinterpret_cast<const uint4*>(qp)[i];
+}
+
 // Running state of one wave: G query heads of one KV head over a run of blocks.
 template <int D, int kFmt>
 struct HeadState {
@@ -210,6 +222,14 @@ struct HeadState {
       if (r < G) w = reinterpret_cast<const uint4*>(qp)[i];
       qop[i] = __builtin_bit_cast(bf16x8_t, w);
     }
+    reset();
+    set_qbias();
+  }
+
+  // Start a run from the words load_query() fetched (lanes r >= G get zeros).
+  __device__ __forceinline__ void begin_loaded(const uint4* qw, int G, int r) {
+#pragma unroll
+    for (int i = 0; i < T::kKSteps; ++i) qop[i] = __builtin_bit_cast(bf16x8_t, r < G ? qw[i] : make_uint4(0, 0, 0, 0));
     reset();
     set_qbias();
   }
