@@ -38,7 +38,7 @@ struct PlannedPending {
 // kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
 // write the output or the partial records.
 template <int D, int kFmt, int kTiles>
-__device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, int g, int lane) {
+__device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, int g, int lane, float* stage) {
   const int r = lane & 15, c = lane >> 4;
   const int ncols = min(it.ncols, 16 * kTiles);
   if (ncols <= 0) return;
@@ -109,6 +109,11 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
     }
   }
 
+  // Results leave through this wave's LDS stage, kStageRows columns per
+  // pass, as whole 16-byte pieces with consecutive lanes on consecutive
+  // pieces (each lane holds a 16-byte-strided run of one column).  Records
+  // of a KV head are adjacent, so an item's records are consecutive rows; an
+  // output row's address comes from the lane that owns its column.
   const int d0 = (D / 4) * c;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
@@ -116,15 +121,32 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
     const float L = hs[t].total_l();
     float o[4 * Tile<D, kFmt>::kE];
     hs[t].unpack(o);
-    if (16 * t + r >= ncols) continue;
-    if (it.rec0 < 0) {
-      store_bf16_run<D>(reinterpret_cast<uint16_t*>(a.out) + row[t] * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
-    } else {
-      const int64_t wr = (int64_t)clampi(it.rec0 + 16 * t + r, 0, a.num_records - 1) * a.num_kv_heads + g;
-      store_f32_run<D>(a.ws_acc + wr * D, d0, o);
-      if (c == 0) {
-        a.ws_m[wr] = hs[t].m;
-        a.ws_l[wr] = L;
+    const int nt = min(16, ncols - 16 * t);                 // live columns of this tile
+    const bool direct = it.rec0 < 0;
+    const int64_t rec_row0 = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t, 0, a.num_records - 1);
+    if (!direct && c == 0 && r < nt) {
+      const int64_t wr = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t + r, 0, a.num_records - 1);
+      a.ws_m[wr] = hs[t].m;
+      a.ws_l[wr] = L;
+    }
+    for (int rr = 0; rr < nt; rr += kStageRows) {
+      const int nr = min(kStageRows, nt - rr);
+      const bool mine = r >= rr && r < rr + nr;
+      wave_lds_sync();                                      // the previous pass's reads are done
+      if (direct) {
+        if (mine) store_bf16_run<D>(reinterpret_cast<uint16_t*>(stage) + (r - rr) * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
+        wave_lds_sync();
+        for (int pc = lane; pc < nr * D / 8; pc += 64) {
+          const int col = rr + pc / (D / 8);
+          const int64_t orow = __shfl(row[t], col, 64);       // lane col holds that column's output row
+          reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + orow * D)[pc % (D / 8)] =
+              reinterpret_cast<const uint4*>(stage)[pc];
+        }
+      } else {
+        if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
+        wave_lds_sync();
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (rec_row0 + rr) * D);
+        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
       }
     }
   }
@@ -136,9 +158,10 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.y * a.waves_per_wg + wave;
   if (g >= a.num_kv_heads) return;
+  extern __shared__ float s_stage[];           // per wave kStageRows x D floats
   const int k0 = clampi(a.wg_start[blockIdx.x], 0, a.num_items);
   const int k1 = clampi(a.wg_start[blockIdx.x + 1], k0, a.num_items);
-  for (int k = k0; k < k1; ++k) run_item<D, kFmt, kTiles>(a, a.items[k], g, lane);
+  for (int k = k0; k < k1; ++k) run_item<D, kFmt, kTiles>(a, a.items[k], g, lane, s_stage + wave * kStageRows * D);
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's
@@ -166,7 +189,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(Pla
       lv[k] = 0.0f;
       av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if (e + k < e1) {
-        const int64_t wr = (int64_t)clampi(a.entries[e + k], 0, a.num_records - 1) * a.num_kv_heads + g;
+        const int64_t wr = (int64_t)g * a.num_records + clampi(a.entries[e + k], 0, a.num_records - 1);
         mv[k] = a.ws_m[wr];
         if (mv[k] != -INFINITY) {
           lv[k] = a.ws_l[wr];
@@ -202,7 +225,8 @@ hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
   const dim3 block(64 * a.waves_per_wg);
   const int f = a.cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (a.cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
   const int tiles = a.max_item_columns > 16 ? 2 : 1;
-#define PA_LAUNCH(D_, F_, T_) hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, 0, stream, a)
+  const size_t lds = (size_t)a.waves_per_wg * kStageRows * a.head_dim * sizeof(float);
+#define PA_LAUNCH(D_, F_, T_) hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, lds, stream, a)
 #define PA_LAUNCH_T(D_, F_) do { if (tiles == 2) PA_LAUNCH(D_, F_, 2); else PA_LAUNCH(D_, F_, 1); } while (0)
   if (a.head_dim == 128) {
     if (f == kFmtFp8) PA_LAUNCH_T(128, kFmtFp8);

@@ -171,17 +171,7 @@ __device__ __forceinline__ int slice_of(int u, int U, int n) {
 // to 16 query heads takes two passes); the stage follows start[] and ctx[]
 // in the dynamic LDS, 16-byte aligned.  LDS per workgroup:
 // 4*(2B+1) + 8 waves * 8 rows * D * 4 bytes <= 32 KB + 32 KB for B <= 4096.
-constexpr int kStageRows = 8;
 __host__ __device__ constexpr int balanced_stage_offset_words(int num_seqs) { return (2 * num_seqs + 1 + 3) / 4 * 4; }
-
-// Make this wave's LDS writes visible to its other lanes' later LDS reads
-// (and finish its reads before later writes): wait for the wave's LDS
-// operations, and keep the compiler from moving LDS accesses across.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0); vmcnt and expcnt left alone
-  __builtin_amdgcn_wave_barrier();
-}
 
 struct UnitIds {
   int b, i, blk;       // lane j: the (sequence, logical block, raw table entry) of unit base + j

@@ -422,6 +422,18 @@ struct HeadState {
   }
 };
 
+// Finished rows leave a wave through LDS, this many rows per pass.
+constexpr int kStageRows = 8;
+
+// Make this wave's LDS writes visible to its other lanes' later LDS reads
+// (and finish its reads before later writes): wait for the wave's LDS
+// operations, and keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Write D/4 normalised values of one query row as bf16 (16-byte stores).
 template <int D>
 __device__ __forceinline__ void store_bf16_run(uint16_t* dst_row, int d0, const float* o, float inv) {

@@ -151,7 +151,8 @@ inline PlanLayout plan_layout(const pa_plan_info& info) {
   return l;
 }
 
-// Records: [num_records, num_kv_heads] rows of m, l (floats) and acc[head_dim].
+// Records: [num_kv_heads, num_records] rows of m, l (floats) and acc[head_dim]
+// (one KV head's records adjacent, so a wave's columns are consecutive rows).
 inline size_t planned_workspace_bytes(const pa_plan_info& info) {
   const size_t rows = (size_t)info.num_records * info.num_kv_heads;
   if (rows == 0) return 0;
