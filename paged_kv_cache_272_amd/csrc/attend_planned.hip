@@ -31,83 +31,136 @@ template <int D, int kFmt>
 struct PlannedPending {
   BlockRegs<D, kFmt> regs;
   int i;              // logical block
+  bool live;          // false: a fetch past the item's end (a copy of its last block, folded in as a no-op)
   float ks, vs;
 };
 
-// One plan item on one wave (KV head g): stream the item's blocks through
-// kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
-// write the output or the partial records.
-template <int D, int kFmt, int kTiles>
-__device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, int g, int lane, float* stage) {
-  const int r = lane & 15, c = lane >> 4;
-  const int ncols = min(it.ncols, 16 * kTiles);
-  if (ncols <= 0) return;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int seq = clampi(it.seq, 0, a.num_seqs - 1);
+// This lane's query column of each tile of an item (columns past ncols are
+// zero and see nothing).  Every lane loads (a clamped index) so that the
+// number of loads does not depend on the lanes; the loaded values are only
+// zeroed where used (run_item).
+template <int kTiles>
+__device__ __forceinline__ void load_item_columns(const PlannedArgs& a, int col0, int r, PlanColumn (&cols)[kTiles]) {
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) cols[t] = a.cols[clampi(col0 + 16 * t + r, 0, a.num_columns - 1)];
+}
 
-  // this lane's query column in each tile (columns past ncols are zero and see nothing)
-  int horizon[kTiles];
-  int64_t row[kTiles];
-  HeadState<D, kFmt> hs[kTiles];
+// Wait for loads into these registers here (not where the compiler would
+// first copy them).
+__device__ __forceinline__ void settle_reg(int& v) { asm volatile("" : "+v"(v)); }
+template <int kTiles>
+__device__ __forceinline__ void settle_cols(PlanColumn (&cols)[kTiles]) {
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
-    PlanColumn col{0, 0, 0, 0};
-    const bool live = 16 * t + r < ncols;
-    if (live) col = a.cols[clampi(it.col0 + 16 * t + r, 0, a.num_columns - 1)];
-    horizon[t] = col.horizon;
-    row[t] = (int64_t)clampi(col.q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
-             clampi(col.j, 0, G - 1);
-    hs[t].begin_row(reinterpret_cast<const uint16_t*>(a.q), live ? row[t] : -1, c);
+    settle_reg(cols[t].q_row);
+    settle_reg(cols[t].j);
+    settle_reg(cols[t].horizon);
   }
-  const bool second = kTiles > 1 && ncols > 16;     // wave-uniform
+}
 
+// What a wave needs of the item after the current one, loaded while the
+// current one runs: its columns and the physical ids of its first 64 blocks.
+template <int kTiles>
+struct NextItem {
+  PlanColumn cols[kTiles];
+  int blk;              // lane j: physical id of block blk_lo + j
+};
+
+template <int kTiles>
+__device__ __forceinline__ void load_next(const PlannedArgs& a, const PlanItem& it, int lane, NextItem<kTiles>& nx) {
+  load_item_columns<kTiles>(a, it.col0, lane & 15, nx.cols);
+  const int seq = clampi(it.seq, 0, a.num_seqs - 1);
+  const int lo = max(it.blk_lo, 0);
+  // every lane loads (an entry inside the table row); lanes past the item's blocks are never read out
+  nx.blk = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + clampi(lo + lane, 0, a.max_blocks_per_seq - 1)];
+}
+
+// One plan item on one wave (KV head g): stream the item's blocks through
+// kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
+// write the output or the partial records.  `cur` holds the item's columns
+// and first block ids (loaded during the previous item); those of `next_it`
+// (the following item, or this one again after the last) are loaded into
+// `nx` once this item's own loads are issued, on every path alike.
+//
+// Vector memory operations complete in issue order and each wait is a count
+// the compiler fixes per program point from the path with the fewest
+// operations issued after the awaited one, so the block loop issues the same
+// loads on every path (one loop exit; past the item's end a dead copy of its
+// last block) and the wait before a block leaves the next block in flight.
+template <int D, int kFmt, int kTiles>
+__device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, const NextItem<kTiles>& cur,
+                                         const PlanItem& next_it, NextItem<kTiles>& nx, int g, int lane,
+                                         float* stage) {
+  const int r = lane & 15, c = lane >> 4;
+  const int ncols = min(it.ncols, 16 * kTiles);
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int seq = clampi(it.seq, 0, a.num_seqs - 1);
   const int lo = max(it.blk_lo, 0), hi = min(it.blk_hi, a.max_blocks_per_seq);
   const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
 
-  // physical ids and fp8 scales of 64 blocks at a time: lane j holds block idbase + j
-  int idbase = lo - 64, my_blk = 0;
-  float my_ks = 1.0f, my_vs = 1.0f;
+  int horizon[kTiles];
+  int64_t row[kTiles];
+  HeadState<D, kFmt> hs[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const bool live = 16 * t + r < ncols;
+    horizon[t] = live ? cur.cols[t].horizon : 0;
+    row[t] = live ? (int64_t)clampi(cur.cols[t].q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
+                        clampi(cur.cols[t].j, 0, G - 1)
+                  : 0;
+    hs[t].begin_row(reinterpret_cast<const uint16_t*>(a.q), live ? row[t] : -1, c);
+  }
+  load_next<kTiles>(a, next_it, lane, nx);
+  const bool second = kTiles > 1 && ncols > 16;     // wave-uniform
+
+  // physical ids of 64 blocks at a time (lane j: block idbase + j)
+  int idbase = lo, my_blk = cur.blk;
   auto fetch = [&](PlannedPending<D, kFmt>& p, int i) {
+    p.live = i < hi;
+    i = min(i, hi - 1);
     if (i - idbase >= 64) {
+      // a new chunk of ids, waited for here (once per 64 blocks)
       idbase += 64;
-      const int bi = idbase + lane;
-      my_blk = bi < hi ? clampi(table[bi], 0, a.num_blocks - 1) : 0;
-      if constexpr (kFmt != kFmtBf16) {
-        my_ks = bi < hi ? a.k_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
-        my_vs = bi < hi ? a.v_scale[(int64_t)my_blk * a.num_kv_heads + g] : 1.0f;
-      }
+      my_blk = table[clampi(idbase + lane, 0, a.max_blocks_per_seq - 1)];
+      settle_reg(my_blk);
     }
-    const int j = i - idbase;
     p.i = i;
+    const int64_t blk = clampi(__builtin_amdgcn_readlane(my_blk, i - idbase), 0, a.num_blocks - 1);
     if constexpr (kFmt != kFmtBf16) {
-      p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), j));
-      p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), j));
+      p.ks = a.k_scale[blk * a.num_kv_heads + g];
+      p.vs = a.v_scale[blk * a.num_kv_heads + g];
     } else {
       p.ks = p.vs = 1.0f;
     }
-    load_block<D, kFmt>(p.regs, kbase, vbase, __builtin_amdgcn_readlane(my_blk, j), a.num_kv_heads, g, r, c);
+    load_block<D, kFmt>(p.regs, kbase, vbase, blk, a.num_kv_heads, g, r, c);
+    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the next consume's waits
   };
   auto consume = [&](const PlannedPending<D, kFmt>& p) {
     const int t0 = p.i * kBlockTokens;
-    const int valid = min(kBlockTokens, it.kv_len - t0);
+    // a dead copy sees no token: the running max, sum and accumulator stay as they are
+    const int valid = p.live ? min(kBlockTokens, it.kv_len - t0) : 0;
     hs[0].step_cols(p.regs, valid, horizon[0] - t0, a.scale_log2 * p.ks, p.vs, c);
     if constexpr (kTiles > 1)
       if (second) hs[1].step_cols(p.regs, valid, horizon[1] - t0, a.scale_log2 * p.ks, p.vs, c);
   };
 
-  // software pipeline: the next block's loads are in flight while this one computes
-  PlannedPending<D, kFmt> p0, p1;
-  if (lo < hi) fetch(p0, lo);
-  for (int i = lo; i < hi; i += 2) {
-    if (i + 1 < hi) fetch(p1, i + 1);
-    consume(p0);
-    if (i + 1 < hi) {
-      if (i + 2 < hi) fetch(p0, i + 2);
+  // two blocks in flight
+  if (lo < hi) {
+    PlannedPending<D, kFmt> p0, p1;
+    fetch(p0, lo);
+    for (int i = lo; i < hi; i += 2) {
+      fetch(p1, i + 1);
+      consume(p0);
+      fetch(p0, i + 2);
       consume(p1);
     }
   }
+  // the next item's loads have long landed: take their wait here
+  settle_cols<kTiles>(nx.cols);
+  settle_reg(nx.blk);
+  if (ncols <= 0) return;
 
   // Results leave through this wave's LDS stage, kStageRows columns per
   // pass, as whole 16-byte pieces with consecutive lanes on consecutive
@@ -161,7 +214,47 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
   extern __shared__ float s_stage[];           // per wave kStageRows x D floats
   const int k0 = clampi(a.wg_start[blockIdx.x], 0, a.num_items);
   const int k1 = clampi(a.wg_start[blockIdx.x + 1], k0, a.num_items);
-  for (int k = k0; k < k1; ++k) run_item<D, kFmt, kTiles>(a, a.items[k], g, lane, s_stage + wave * kStageRows * D);
+  if (k0 >= k1) return;
+  float* stage = s_stage + wave * kStageRows * D;
+  // item headers, 64 at a time: lane j holds item kb + j
+  int kb = k0;
+  PlanItem mine{0, 0, 0, 0, 0, 0, -1, 0};
+  auto load_headers = [&]() {
+    if (kb + lane < k1) mine = a.items[kb + lane];
+    settle_reg(mine.seq);
+    settle_reg(mine.blk_lo);
+    settle_reg(mine.blk_hi);
+    settle_reg(mine.col0);
+    settle_reg(mine.ncols);
+    settle_reg(mine.kv_len);
+    settle_reg(mine.rec0);
+  };
+  auto header = [&](int k) {
+    const int j = k - kb;
+    return PlanItem{__builtin_amdgcn_readlane(mine.seq, j),  __builtin_amdgcn_readlane(mine.blk_lo, j),
+                    __builtin_amdgcn_readlane(mine.blk_hi, j), __builtin_amdgcn_readlane(mine.col0, j),
+                    __builtin_amdgcn_readlane(mine.ncols, j),  __builtin_amdgcn_readlane(mine.kv_len, j),
+                    __builtin_amdgcn_readlane(mine.rec0, j),   0};
+  };
+  load_headers();
+  PlanItem it = header(k0);
+  NextItem<kTiles> cur, nx;
+  load_next<kTiles>(a, it, lane, cur);
+  settle_cols<kTiles>(cur.cols);        // (the item loop then finds them settled on every path)
+  settle_reg(cur.blk);
+  for (int k = k0; k < k1; ++k) {
+    PlanItem next_it = it;
+    if (k + 1 < k1) {
+      if (k + 1 - kb >= 64) {
+        kb += 64;
+        load_headers();
+      }
+      next_it = header(k + 1);
+    }
+    run_item<D, kFmt, kTiles>(a, it, cur, next_it, nx, g, lane, stage);
+    it = next_it;
+    cur = nx;
+  }
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's

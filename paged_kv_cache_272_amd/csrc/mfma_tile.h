@@ -211,6 +211,7 @@ struct HeadState {
   f32x4_t acc[kE];
   float m, l;
   float qbias;   // int4: 136 * (sum of this lane's query column): removed from every logit
+  bool qbias_pending = false;   // int4: qbias still to be taken (begin_row)
   float vbias;   // int4: sum over blocks of V scale * (sum of the block's bf16 P), rescaled like acc
 
   // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
@@ -235,17 +236,16 @@ struct HeadState {
   }
 
   // Q^T operand with an arbitrary query row per column: lane r takes row
-  // `row` (-1: a zero column).
+  // `row`; a column that will see no token (every step masks it whole) may
+  // pass -1 and gets row 0.  Every lane issues the same loads and nothing
+  // here uses their values, so they are waited for at the first step (the
+  // int4 query sum is taken there too).
   __device__ __forceinline__ void begin_row(const uint16_t* q, int64_t row, int c) {
     const uint16_t* qp = q + (row < 0 ? 0 : row) * D + (D / 4) * c;
 #pragma unroll
-    for (int i = 0; i < T::kKSteps; ++i) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (row >= 0) w = reinterpret_cast<const uint4*>(qp)[i];
-      qop[i] = __builtin_bit_cast(bf16x8_t, w);
-    }
+    for (int i = 0; i < T::kKSteps; ++i) qop[i] = __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4*>(qp)[i]);
     reset();
-    set_qbias();
+    qbias_pending = true;
   }
 
   // int4: 136 times the column's query sum (the 4 lane groups hold D/4 each)
@@ -307,6 +307,12 @@ struct HeadState {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
     }
     // int4: the MFMA saw values + 136; remove 136 * (query sum) before scaling
+    if constexpr (kInt4) {
+      if (qbias_pending) {
+        set_qbias();
+        qbias_pending = false;
+      }
+    }
     const float sb = -qbias * sc;
     float sv[4];
 #pragma unroll

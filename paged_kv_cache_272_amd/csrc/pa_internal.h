@@ -168,11 +168,13 @@ struct PlannedArgs {
   const float* k_scale;
   const float* v_scale;
   const int32_t* block_tables;
-  const PlanItem* items;
-  const PlanColumn* cols;
-  const PlanMergeRow* rows;
-  const int32_t* entries;
-  const int32_t* wg_start;
+  // the plan arrays are read-only and alias nothing the kernels write, so
+  // their wave-uniform reads can go through scalar loads
+  const PlanItem* __restrict__ items;
+  const PlanColumn* __restrict__ cols;
+  const PlanMergeRow* __restrict__ rows;
+  const int32_t* __restrict__ entries;
+  const int32_t* __restrict__ wg_start;
   float* ws_m;
   float* ws_l;
   float* ws_acc;
