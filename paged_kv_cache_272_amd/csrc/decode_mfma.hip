@@ -174,7 +174,8 @@ __device__ __forceinline__ int slice_of(int u, int U, int n) {
 __host__ __device__ constexpr int balanced_stage_offset_words(int num_seqs) { return (2 * num_seqs + 1 + 3) / 4 * 4; }
 
 struct UnitIds {
-  int b, i, blk;       // lane j: the (sequence, logical block, raw table entry) of unit base + j
+  int b, i, blk;       // lane j: the (sequence, logical block, physical block) of unit base + j
+  float ks, vs;        // e4m3/int4: that block's scales for this wave's head
 };
 
 __device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int u) {
@@ -188,25 +189,37 @@ __device__ __forceinline__ int find_sequence(const int* start, int num_seqs, int
   return lo;
 }
 
-// Table entries of 64 units, one per lane, waited for here: a register
-// holding a load still in flight cannot be copied without a wait, and the
-// compiler copies these ids across loop iterations.  One wait per 64 units.
-__device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int lane) {
-  UnitIds id{0, 0, 0};
+// Table entries (and block scales) of 64 units, one per lane, waited for
+// here: a register holding a load still in flight cannot be copied without a
+// wait, and the compiler copies these ids across loop iterations.  One or
+// two waits per 64 units.
+template <bool kScaled>
+__device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* start, int base, int u1, int g, int lane) {
+  UnitIds id{0, 0, 0, 1.0f, 1.0f};
   const int u = base + lane;
   if (u < u1) {
     id.b = find_sequence(start, a.num_seqs, u);
     id.i = u - start[id.b];
-    id.blk = a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i];
+    id.blk = clamp_block(a.block_tables[(int64_t)id.b * a.max_blocks_per_seq + id.i], a.num_blocks);
+    if constexpr (kScaled) {
+      id.ks = a.k_scale[(int64_t)id.blk * a.num_kv_heads + g];
+      id.vs = a.v_scale[(int64_t)id.blk * a.num_kv_heads + g];
+    }
   }
   asm volatile("" : "+v"(id.blk));
+  if constexpr (kScaled) asm volatile("" : "+v"(id.ks), "+v"(id.vs));
   return id;
 }
 
 template <int D, int kFmt>
 struct Pending {
+  // bf16 caches: the query rows of the unit's sequence come with every unit
+  // (load_query; used when the unit starts the sequence).  e4m3/int4 blocks
+  // are small enough that those four extra loads per unit cost more than
+  // loading the query when a sequence starts.
+  static constexpr bool kQueryInFetch = kFmt == kFmtBf16;
   BlockRegs<D, kFmt> regs;
-  uint4 q[D / 32];          // query rows of the unit's sequence (load_query), used when the unit starts it
+  uint4 q[kQueryInFetch ? D / 32 : 1];
   int64_t blk;
   int b, i, ctx;
   float ks, vs;
@@ -357,17 +370,17 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
 
   // Table entries of the current 64-unit chunk.
   int base = u0;
-  UnitIds cur = unit_ids(a, s_start, base, u1, lane);
+  UnitIds cur = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base, u1, g, lane);
 
   // Vector memory operations complete in issue order and are waited for by
   // a count the compiler fixes per program point, taking the path with the
   // fewest operations issued after the awaited one.  So everything a unit
   // needs is loaded in fetch() (a load issued at consume time, after the
   // other unit's block, would make this wait for that block), and fetch()
-  // issues the same loads on every path: the query rows of the unit's
-  // sequence come with every unit (cache hits after its first), not only
-  // with the unit that starts the sequence.  Only the e4m3/int4 new-token
-  // runs are conditional (once per sequence).
+  // issues the same loads on every path: for bf16 the query rows of the
+  // unit's sequence come with every unit (cache hits after its first), not
+  // only with the unit that starts the sequence.  The e4m3/int4 paths take
+  // their query (and new-token runs) once per sequence instead.
   constexpr bool kScaled = kFmt != kFmtBf16;
   Staging<D> st;
   int fetched_b = -1;
@@ -385,16 +398,16 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
     u = min(u, u1 - 1);
     if (u - base >= 64) {
       base += 64;
-      cur = unit_ids(a, s_start, base, u1, lane);
+      cur = unit_ids<(kFmt != kFmtBf16)>(a, s_start, base, u1, g, lane);
     }
     const int j = u - base;
     p.b = __builtin_amdgcn_readlane(cur.b, j);
     p.i = __builtin_amdgcn_readlane(cur.i, j);
-    p.blk = clamp_block(__builtin_amdgcn_readlane(cur.blk, j), a.num_blocks);
+    p.blk = __builtin_amdgcn_readlane(cur.blk, j);
     p.ctx = s_ctx[p.b];
     p.starts = p.b != fetched_b;
     fetched_b = p.b;
-    load_query<D>(q, q_row(p.b), G, r, c, p.q);
+    if constexpr (Pending<D, kFmt>::kQueryInFetch) load_query<D>(q, q_row(p.b), G, r, c, p.q);
     // appending: the sequence's last block holds its newest token
     p.off = p.live && a.append && (p.i + 1) * kBlockTokens >= p.ctx ? (p.ctx - 1) % kBlockTokens : -1;
     p.row_staged = false;
@@ -403,8 +416,8 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
         st.row_busy = p.row_staged = true;
         load_new_runs(p.b, st.nk, st.nv);
       }
-      p.ks = a.k_scale[p.blk * a.num_kv_heads + g];
-      p.vs = a.v_scale[p.blk * a.num_kv_heads + g];
+      p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
+      p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
       load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
     } else {
       p.ks = p.vs = 1.0f;
@@ -451,7 +464,21 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_k
     if (p.starts) {
       if (cur_b >= 0) finish(cur_b);
       cur_b = p.b;
-      hs.begin_loaded(p.q, G, r);
+      if constexpr (Pending<D, kFmt>::kQueryInFetch) {
+        hs.begin_loaded(p.q, G, r);
+      } else {
+        // load the query now and wait here: this drains the other unit's
+        // block too, once per sequence start
+        uint4 qw[D / 32];
+        load_query<D>(q, q_row(p.b), G, r, c, qw);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+          uint32_t x = qw[i].x, y = qw[i].y, z = qw[i].z, w = qw[i].w;
+          asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+          qw[i] = make_uint4(x, y, z, w);
+        }
+        hs.begin_loaded(qw, G, r);
+      }
     }
     if (p.off >= 0) {
       if (!kScaled || p.row_staged) {
