@@ -53,7 +53,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("num_q_tokens", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
                 ("head_dim", _i32), ("num_items", _i32), ("num_columns", _i32), ("num_records", _i32),
                 ("num_merge_rows", _i32), ("num_merge_entries", _i32), ("num_shared_groups", _i32),
-                ("num_wgs", _i32), ("max_item_columns", _i32), ("reserved", _i32), ("plan_bytes", _i64),
+                ("num_wgs", _i32), ("max_item_columns", _i32), ("num_wide_groups", _i32), ("plan_bytes", _i64),
                 ("workspace_bytes", _i64), ("block_reads", _i64)]
 
     def as_dict(self) -> dict:

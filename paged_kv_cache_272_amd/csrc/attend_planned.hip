@@ -75,6 +75,56 @@ __device__ __forceinline__ void load_next(const PlannedArgs& a, const PlanItem& 
   nx.blk = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + clampi(lo + lane, 0, a.max_blocks_per_seq - 1)];
 }
 
+// Results of an item's tiles leave through this wave's LDS stage,
+// kStageRows columns per pass, as whole 16-byte pieces with consecutive
+// lanes on consecutive pieces (each lane holds a 16-byte-strided run of one
+// column).  Records of a KV head are adjacent, so an item's records are
+// consecutive rows; an output row's address comes from the lane that owns
+// its column.
+template <int D, int kFmt, int kTiles>
+__device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const PlanItem& it,
+                                                 const HeadState<D, kFmt> (&hs)[kTiles], const int64_t (&row)[kTiles],
+                                                 int ncols, bool second, int g, int lane, float* stage) {
+  const int r = lane & 15, c = lane >> 4;
+  const int d0 = (D / 4) * c;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    if (t > 0 && !second) break;
+    const float L = hs[t].total_l();
+    float o[4 * Tile<D, kFmt>::kE];
+    hs[t].unpack(o);
+    const int nt = min(16, ncols - 16 * t);                 // live columns of this tile
+    const bool direct = it.rec0 < 0 || a.num_records <= 0;   // (no workspace: a plan not built here)
+    // the tile's nt records stay inside this head's records even for a plan that was not built here
+    const int64_t rec_row0 = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t, 0, max(a.num_records - nt, 0));
+    if (!direct && c == 0 && r < nt) {
+      const int64_t wr = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t + r, 0, a.num_records - 1);
+      a.ws_m[wr] = hs[t].m;
+      a.ws_l[wr] = L;
+    }
+    for (int rr = 0; rr < nt; rr += kStageRows) {
+      const int nr = min(kStageRows, nt - rr);
+      const bool mine = r >= rr && r < rr + nr;
+      wave_lds_sync();                                      // the previous pass's reads are done
+      if (direct) {
+        if (mine) store_bf16_run<D>(reinterpret_cast<uint16_t*>(stage) + (r - rr) * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
+        wave_lds_sync();
+        for (int pc = lane; pc < nr * D / 8; pc += 64) {
+          const int col = rr + pc / (D / 8);
+          const int64_t orow = __shfl(row[t], col, 64);       // lane col holds that column's output row
+          reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + orow * D)[pc % (D / 8)] =
+              reinterpret_cast<const uint4*>(stage)[pc];
+        }
+      } else {
+        if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
+        wave_lds_sync();
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (rec_row0 + rr) * D);
+        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
+      }
+    }
+  }
+}
+
 // One plan item on one wave (KV head g): stream the item's blocks through
 // kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
 // write the output or the partial records.  `cur` holds the item's columns
@@ -141,9 +191,10 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
     const int t0 = p.i * kBlockTokens;
     // a dead copy sees no token: the running max, sum and accumulator stay as they are
     const int valid = p.live ? min(kBlockTokens, it.kv_len - t0) : 0;
-    hs[0].step_cols(p.regs, valid, horizon[0] - t0, a.scale_log2 * p.ks, p.vs, c);
+    const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(p.regs, valid, c);
+    hs[0].step_cols(p.regs, vo, valid, horizon[0] - t0, a.scale_log2 * p.ks, p.vs, c);
     if constexpr (kTiles > 1)
-      if (second) hs[1].step_cols(p.regs, valid, horizon[1] - t0, a.scale_log2 * p.ks, p.vs, c);
+      if (second) hs[1].step_cols(p.regs, vo, valid, horizon[1] - t0, a.scale_log2 * p.ks, p.vs, c);
   };
 
   // two blocks in flight
@@ -162,47 +213,7 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   settle_reg(nx.blk);
   if (ncols <= 0) return;
 
-  // Results leave through this wave's LDS stage, kStageRows columns per
-  // pass, as whole 16-byte pieces with consecutive lanes on consecutive
-  // pieces (each lane holds a 16-byte-strided run of one column).  Records
-  // of a KV head are adjacent, so an item's records are consecutive rows; an
-  // output row's address comes from the lane that owns its column.
-  const int d0 = (D / 4) * c;
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    if (t > 0 && !second) break;
-    const float L = hs[t].total_l();
-    float o[4 * Tile<D, kFmt>::kE];
-    hs[t].unpack(o);
-    const int nt = min(16, ncols - 16 * t);                 // live columns of this tile
-    const bool direct = it.rec0 < 0;
-    const int64_t rec_row0 = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t, 0, a.num_records - 1);
-    if (!direct && c == 0 && r < nt) {
-      const int64_t wr = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t + r, 0, a.num_records - 1);
-      a.ws_m[wr] = hs[t].m;
-      a.ws_l[wr] = L;
-    }
-    for (int rr = 0; rr < nt; rr += kStageRows) {
-      const int nr = min(kStageRows, nt - rr);
-      const bool mine = r >= rr && r < rr + nr;
-      wave_lds_sync();                                      // the previous pass's reads are done
-      if (direct) {
-        if (mine) store_bf16_run<D>(reinterpret_cast<uint16_t*>(stage) + (r - rr) * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
-        wave_lds_sync();
-        for (int pc = lane; pc < nr * D / 8; pc += 64) {
-          const int col = rr + pc / (D / 8);
-          const int64_t orow = __shfl(row[t], col, 64);       // lane col holds that column's output row
-          reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + orow * D)[pc % (D / 8)] =
-              reinterpret_cast<const uint4*>(stage)[pc];
-        }
-      } else {
-        if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
-        wave_lds_sync();
-        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (rec_row0 + rr) * D);
-        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
-      }
-    }
-  }
+  store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, stage);
 }
 
 // Workgroup x runs the items of slice x in order, one wave per KV head.
@@ -255,6 +266,158 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
     it = next_it;
     cur = nx;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Wide groups: workgroup (group, KV head g), wave w runs item item0 + w of
+// the group (up to two 16-column tiles).  The group's items share their
+// sequence and first block, so every block of the group's run is read from
+// memory once, by the whole workgroup, into LDS, and each wave folds it into
+// its own tiles from there: the 8 tiles of a prefill chunk cost one read of
+// each block instead of eight.  Blocks alternate between two LDS buffers:
+// block i+1 is loaded into registers while block i is folded in, then
+// written to the other buffer before the barrier that ends the step.
+
+template <int D, int kFmt>
+struct WideLayout {
+  static constexpr int kRowBytes = D * Tile<D, kFmt>::kBits / 8;       // one token row of one head
+  static constexpr int kStride = kRowBytes + 16;                       // padded: rows on different banks
+  static constexpr int kHalf = kBlockTokens * kStride;                 // K (or V) of one block
+  static constexpr int kBuf = 2 * kHalf;                               // K then V
+  static constexpr int kPiecesPerRow = kRowBytes / 16;
+  static constexpr int kPieces = 2 * kBlockTokens * kPiecesPerRow;     // 16-byte pieces per block, K and V
+  static_assert(kPieces <= 64 * kWideTiles, "one piece per thread");
+};
+
+// The register layout of load_block, read from a block staged in LDS.
+template <int D, int kFmt>
+__device__ __forceinline__ void load_block_lds(BlockRegs<D, kFmt>& br, const uint8_t* buf, int r, int c) {
+  using T = Tile<D, kFmt>;
+  using L = WideLayout<D, kFmt>;
+  constexpr int kKOff = (D / 4) * T::kBits / 8, kVOff = T::kE * T::kBits / 8;
+  load_words<T::kKWords>(buf + r * L::kStride + kKOff * c, br.k);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) load_words<T::kVWords>(buf + L::kHalf + (4 * c + e) * L::kStride + kVOff * r, br.v[e]);
+}
+
+template <int D, int kFmt>
+__global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArgs a) {
+  constexpr int kTiles = 2;
+  using L = WideLayout<D, kFmt>;
+  extern __shared__ __align__(16) uint8_t s_wide[];          // 2 block buffers, then the waves' result stages
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int g = blockIdx.y;
+  const PlanWideGroup grp = a.wide[blockIdx.x];
+  const int nitems = clampi(grp.nitems, 0, kWideTiles);
+  if (nitems == 0) return;                                   // (every wave of the workgroup)
+  const int k0 = clampi(grp.item0, 0, a.num_items - 1);
+  const PlanItem first = a.items[k0];
+  const int seq = clampi(first.seq, 0, a.num_seqs - 1);
+  const int lo = max(grp.blk_lo, 0), hi = min(grp.blk_hi, a.max_blocks_per_seq);
+  const bool has_item = wave < nitems;
+  const PlanItem it = a.items[clampi(grp.item0 + min(wave, nitems - 1), 0, a.num_items - 1)];
+  const int it_hi = min(it.blk_hi, hi);
+  const int ncols = has_item ? min(it.ncols, 16 * kTiles) : 0;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  float* stage = reinterpret_cast<float*>(s_wide + 2 * L::kBuf) + wave * kStageRows * D;
+
+  // this wave's columns and query rows
+  PlanColumn cols[kTiles];
+  load_item_columns<kTiles>(a, it.col0, r, cols);
+  int horizon[kTiles];
+  int64_t row[kTiles];
+  HeadState<D, kFmt> hs[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const bool live = 16 * t + r < ncols;
+    horizon[t] = live ? cols[t].horizon : 0;
+    row[t] = live ? (int64_t)clampi(cols[t].q_row, 0, a.num_q_tokens - 1) * a.num_q_heads + (int64_t)g * G +
+                        clampi(cols[t].j, 0, G - 1)
+                  : 0;
+    hs[t].begin_row(reinterpret_cast<const uint16_t*>(a.q), live ? row[t] : -1, c);
+  }
+  const bool second = ncols > 16;
+
+  // physical ids and scales of 64 blocks at a time (lane j: block idbase + j), in every wave
+  int idbase = lo, my_blk = 0;
+  float my_ks = 1.0f, my_vs = 1.0f;
+  auto load_ids = [&]() {
+    my_blk = clampi(table[clampi(idbase + lane, 0, a.max_blocks_per_seq - 1)], 0, a.num_blocks - 1);
+    if constexpr (kFmt != kFmtBf16) {
+      my_ks = a.k_scale[(int64_t)my_blk * a.num_kv_heads + g];
+      my_vs = a.v_scale[(int64_t)my_blk * a.num_kv_heads + g];
+      asm volatile("" : "+v"(my_ks), "+v"(my_vs));
+    }
+    asm volatile("" : "+v"(my_blk));
+  };
+  load_ids();
+
+  // This thread's 16-byte piece of a block: K rows first, then V rows.
+  // Threads past the pieces load piece 0 and drop it, so every wave issues
+  // one load per block.
+  const bool loader = tid < L::kPieces;
+  const int half = loader && tid >= L::kPieces / 2 ? 1 : 0;
+  const int pidx = loader ? tid - half * (L::kPieces / 2) : 0;
+  const int prow = pidx / L::kPiecesPerRow, pcol = pidx % L::kPiecesPerRow;
+  const int lds_off = half * L::kHalf + prow * L::kStride + pcol * 16;
+  auto load_piece = [&](int i) {
+    if (i - idbase >= 64) {
+      idbase += 64;
+      load_ids();
+    }
+    const int64_t blk = __builtin_amdgcn_readlane(my_blk, i - idbase);
+    const int64_t head_row0 = (blk * a.num_kv_heads + g) * kBlockTokens;
+    return *reinterpret_cast<const uint4*>((half ? vbase : kbase) + (head_row0 + prow) * L::kRowBytes + pcol * 16);
+  };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // this wave's LDS writes and reads are done (lgkmcnt(0))
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // kAhead blocks in flight per thread (a ring of pieces), two LDS buffers.
+  // Step i folds block i in from LDS, having issued the load of block
+  // i + kAhead, and writes block i + 1 (loaded kAhead - 1 steps ago) to the
+  // other buffer.  Every step issues exactly one load (past the run's end a
+  // copy of its last block) so the waits before the writes leave the later
+  // loads in flight.
+  constexpr int kAhead = 4;
+  if (lo < hi) {
+    uint4 ring[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) ring[k] = load_piece(min(lo + k, hi - 1));
+    if (loader) *reinterpret_cast<uint4*>(s_wide + lds_off) = ring[0];
+    lds_barrier();
+    for (int i0 = lo; i0 < hi; i0 += kAhead) {
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) {
+        const int i = i0 + k;
+        ring[k] = load_piece(min(i + kAhead, hi - 1));
+        if (i < hi && has_item && i < it_hi) {
+          BlockRegs<D, kFmt> br;
+          load_block_lds<D, kFmt>(br, s_wide + ((i - lo) & 1) * L::kBuf, r, c);
+          float ks = 1.0f, vs = 1.0f;
+          if constexpr (kFmt != kFmtBf16) {
+            ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i - idbase));
+            vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i - idbase));
+          }
+          const int t0 = i * kBlockTokens;
+          const int valid = min(kBlockTokens, it.kv_len - t0);
+          const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(br, valid, c);
+          hs[0].step_cols(br, vo, valid, horizon[0] - t0, a.scale_log2 * ks, vs, c);
+          if (second) hs[1].step_cols(br, vo, valid, horizon[1] - t0, a.scale_log2 * ks, vs, c);
+        }
+        if (i + 1 < hi && loader)
+          *reinterpret_cast<uint4*>(s_wide + ((i + 1 - lo) & 1) * L::kBuf + lds_off) = ring[(k + 1) % kAhead];
+        lds_barrier();
+      }
+    }
+  }
+  if (!has_item || ncols <= 0) return;
+  store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, stage);
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's
@@ -330,6 +493,30 @@ hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
     else PA_LAUNCH_T(64, kFmtBf16);
   }
 #undef PA_LAUNCH_T
+#undef PA_LAUNCH
+  return hipGetLastError();
+}
+
+// LDS of a wide workgroup: two block buffers, then a result stage per wave.
+template <int D, int kFmt>
+size_t wide_lds_bytes() {
+  return 2 * (size_t)WideLayout<D, kFmt>::kBuf + (size_t)kWideTiles * kStageRows * D * sizeof(float);
+}
+
+hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_wide_groups, a.num_kv_heads);
+  const dim3 block(64 * kWideTiles);
+  const int f = a.cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (a.cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
+#define PA_LAUNCH(D_, F_) \
+  hipLaunchKernelGGL((attend_wide_kernel<D_, F_>), grid, block, (wide_lds_bytes<D_, F_>()), stream, a)
+  if (a.head_dim == 128) {
+    if (f == kFmtFp8) PA_LAUNCH(128, kFmtFp8);
+    else if (f == kFmtInt4) PA_LAUNCH(128, kFmtInt4);
+    else PA_LAUNCH(128, kFmtBf16);
+  } else {
+    if (f == kFmtFp8) PA_LAUNCH(64, kFmtFp8);
+    else PA_LAUNCH(64, kFmtBf16);
+  }
 #undef PA_LAUNCH
   return hipGetLastError();
 }

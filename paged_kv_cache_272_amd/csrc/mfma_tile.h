@@ -201,6 +201,62 @@ __device__ __forceinline__ void load_query(const uint16_t* q, int64_t q_row0, in
   for (int i = 0; i < D / 32; ++i) qw[i] = reinterpret_cast<const uint4*>(qp)[i];
 }
 
+// A operands of a block's P.V MFMAs (V^T as bf16, one per d tile), built
+// once per block and shared by every tile of query columns that folds the
+// block in.  Tokens past `valid` get V = 0 by selection (their slots may
+// hold NaN); a full block needs no selection.
+template <int D, int kFmt>
+struct VOperands {
+  short4_t v[Tile<D, kFmt>::kE];
+};
+
+template <int D, int kFmt>
+__device__ __forceinline__ VOperands<D, kFmt> make_voperands(const BlockRegs<D, kFmt>& br, int valid, int c) {
+  using T = Tile<D, kFmt>;
+  uint32_t vw[4][T::kVWords];
+  if (valid < kBlockTokens) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int w = 0; w < T::kVWords; ++w) vw[e][w] = 4 * c + e < valid ? br.v[e][w] : 0u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int w = 0; w < T::kVWords; ++w) vw[e][w] = br.v[e][w];
+  }
+  VOperands<D, kFmt> vo;
+#pragma unroll
+  for (int nn = 0; nn < T::kE; ++nn) {
+    uint32_t lo, hi;
+    if constexpr (kFmt == kFmtInt4) {
+      // nibble nn of each of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code
+      const uint32_t sel = (uint32_t)(nn / 2) | 0x0c00u | ((uint32_t)(4 + nn / 2) << 16) | 0x0c000000u;
+      const uint32_t b01 = __builtin_amdgcn_perm(vw[1][0], vw[0][0], sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(vw[3][0], vw[2][0], sel);
+      lo = ((nn & 1) ? (b01 >> 4) : b01) & 0x000f000fu;
+      hi = ((nn & 1) ? (b23 >> 4) : b23) & 0x000f000fu;
+      lo |= 0x43004300u;
+      hi |= 0x43004300u;
+    } else if constexpr (kFmt == kFmtFp8) {
+      // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
+      const int w = nn / 4, byte = nn % 4;
+      const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
+      const uint32_t c01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+      const uint32_t c23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+      lo = fp8x2_to_bf16x2(c01, false);
+      hi = fp8x2_to_bf16x2(c23, false);
+    } else {
+      const int w = nn / 2;
+      const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+      lo = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+      hi = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+    }
+    vo.v[nn] = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+  }
+  return vo;
+}
+
 // Running state of one wave: G query heads of one KV head over a run of blocks.
 template <int D, int kFmt>
 struct HeadState {
@@ -273,22 +329,24 @@ struct HeadState {
   // (1..16), `sc` = scale*log2(e) (times the block's K scale for e4m3),
   // `vs` = the block's V scale.  Every column sees the same tokens.
   __device__ __forceinline__ void step(const BlockRegs<D, kFmt>& br, int valid, float sc, float vs, int c) {
-    step_impl<false>(br, valid, 0, sc, vs, c);
+    const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(br, valid, c);
+    step_impl<false>(br, vo, valid, 0, sc, vs, c);
   }
 
   // Fold one block in with a causal horizon per column: column r (this
   // lane's) sees only the block's first `col_valid` tokens (any integer;
   // <= 0 hides the whole block, >= 16 hides nothing).  `valid` still bounds
   // the tokens whose V rows hold data.  A column may see no token at all
-  // (then m stays -inf, l = 0, acc = 0).
-  __device__ __forceinline__ void step_cols(const BlockRegs<D, kFmt>& br, int valid, int col_valid, float sc,
-                                            float vs, int c) {
-    step_impl<true>(br, valid, col_valid, sc, vs, c);
+  // (then m stays -inf, l = 0, acc = 0).  `vo`: the block's P.V operands
+  // (make_voperands), shared by every tile that folds this block in.
+  __device__ __forceinline__ void step_cols(const BlockRegs<D, kFmt>& br, const VOperands<D, kFmt>& vo, int valid,
+                                            int col_valid, float sc, float vs, int c) {
+    step_impl<true>(br, vo, valid, col_valid, sc, vs, c);
   }
 
   template <bool kCols>
-  __device__ __forceinline__ void step_impl(const BlockRegs<D, kFmt>& br, int valid, int col_valid, float sc,
-                                            float vs, int c) {
+  __device__ __forceinline__ void step_impl(const BlockRegs<D, kFmt>& br, const VOperands<D, kFmt>& vo, int valid,
+                                            int col_valid, float sc, float vs, int c) {
     // ---- S^T = K . Q^T
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -317,19 +375,18 @@ struct HeadState {
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = kInt4 ? __builtin_fmaf(s[j], sc, sb) : s[j] * sc;
-    uint32_t vmask = 0xfu;                                        // tokens 4c+e kept for P.V (bit e)
     if (valid < kBlockTokens) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (4 * c + j >= valid) sv[j] = -INFINITY;
-      vmask = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vmask |= (4 * c + e < valid) ? (1u << e) : 0u;
     }
     if constexpr (kCols) {
+      // (a block every column sees in full needs no mask: wave-uniform test)
+      if (__ballot(col_valid < kBlockTokens) != 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * c + j >= col_valid) sv[j] = -INFINITY;
+        for (int j = 0; j < 4; ++j)
+          if (4 * c + j >= col_valid) sv[j] = -INFINITY;
+      }
     }
     // ---- online softmax (base 2)
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -362,50 +419,18 @@ struct HeadState {
                        (bf16_bits_to_f32(pbits.y & 0xffffu) + bf16_bits_to_f32(pbits.y >> 16));
       vbias = __builtin_fmaf(sum_xor16(sum_xor32(ps)), vs, vbias);
     }
-    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n).  Masked
-    // tokens get V = 0 by selection (their slots may hold NaN).
-    uint32_t vw[4][T::kVWords];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int w = 0; w < T::kVWords; ++w) vw[e][w] = (vmask >> e & 1u) ? br.v[e][w] : 0u;
+    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n)
 #pragma unroll
     for (int nn = 0; nn < kE; ++nn) {
-      uint32_t lo, hi;
-      if constexpr (kInt4) {
-        // nibble nn of each of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code
-        const uint32_t sel = (uint32_t)(nn / 2) | 0x0c00u | ((uint32_t)(4 + nn / 2) << 16) | 0x0c000000u;
-        const uint32_t b01 = __builtin_amdgcn_perm(vw[1][0], vw[0][0], sel);
-        const uint32_t b23 = __builtin_amdgcn_perm(vw[3][0], vw[2][0], sel);
-        lo = ((nn & 1) ? (b01 >> 4) : b01) & 0x000f000fu;
-        hi = ((nn & 1) ? (b23 >> 4) : b23) & 0x000f000fu;
-        lo |= 0x43004300u;
-        hi |= 0x43004300u;
-      } else if constexpr (kFmt == kFmtFp8) {
-        // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
-        const int w = nn / 4, byte = nn % 4;
-        const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
-        const uint32_t c01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
-        const uint32_t c23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
-        lo = fp8x2_to_bf16x2(c01, false);
-        hi = fp8x2_to_bf16x2(c23, false);
-      } else {
-        const int w = nn / 2;
-        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-        lo = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
-        hi = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
-      }
-      const short4_t vop = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
       if constexpr (T::kScaled) {
-        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo.v[nn], pop, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
         acc[nn] += t * vs;
       } else {
-        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[nn], 0, 0, 0);
+        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo.v[nn], pop, acc[nn], 0, 0, 0);
       }
     }
   }
 
-  // The wave's total sum (the 4 lane groups hold partial sums of one head).
   __device__ __forceinline__ float total_l() const { return sum_xor16(sum_xor32(l)); }
 
   // int4: take the V bias out of acc itself (for callers that read acc directly)

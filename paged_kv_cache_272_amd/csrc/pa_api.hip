@@ -360,7 +360,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   const pa_plan_info& in = *info;
   if (in.num_seqs < 0 || in.num_q_tokens < 0 || in.num_items < 0 || in.num_columns < 0 || in.num_records < 0 ||
       in.num_merge_rows < 0 || in.num_merge_entries < 0 || in.num_wgs < 0 || in.max_item_columns < 0 ||
-      in.max_item_columns > 32)
+      in.max_item_columns > 32 || in.num_wide_groups < 0)
     return PA_ERR_BAD_SHAPE;
   if (in.num_q_heads < 1 || in.num_kv_heads < 1 || in.num_q_heads % in.num_kv_heads) return PA_ERR_BAD_SHAPE;
   if (in.num_q_heads / in.num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
@@ -373,7 +373,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   if ((int64_t)lay.bytes != in.plan_bytes) return PA_ERR_BAD_SHAPE;
   if ((int64_t)planned_workspace_bytes(in) != in.workspace_bytes) return PA_ERR_BAD_SHAPE;
   if (in.num_items == 0 || in.num_seqs == 0 || in.num_q_tokens == 0) return PA_OK;
-  if (in.num_columns < 1 || in.num_wgs < 1) return PA_ERR_BAD_SHAPE;
+  if (in.num_columns < 1 || (in.num_wgs < 1 && in.num_wide_groups < 1)) return PA_ERR_BAD_SHAPE;
   if (in.num_merge_rows > 0 && (in.num_records < 1 || in.num_merge_entries < 1)) return PA_ERR_BAD_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !plan) return PA_ERR_NULL_POINTER;
   if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
@@ -397,6 +397,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   a.rows = reinterpret_cast<const PlanMergeRow*>(p + lay.rows_off);
   a.entries = reinterpret_cast<const int32_t*>(p + lay.entries_off);
   a.wg_start = reinterpret_cast<const int32_t*>(p + lay.wg_off);
+  a.wide = reinterpret_cast<const PlanWideGroup*>(p + lay.wide_off);
   if (ws_need > 0) {
     const size_t rows = (size_t)in.num_records * in.num_kv_heads;
     float* ws = static_cast<float*>(workspace);
@@ -410,6 +411,7 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   a.num_merge_rows = in.num_merge_rows;
   a.num_merge_entries = in.num_merge_entries;
   a.num_wgs = in.num_wgs;
+  a.num_wide_groups = in.num_wide_groups;
   a.max_item_columns = in.max_item_columns;
   a.num_seqs = in.num_seqs;
   a.num_q_tokens = in.num_q_tokens;
@@ -426,7 +428,8 @@ PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, cons
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   TimingRecord* rec = timing_slot();
   if (rec) (void)hipEventRecord(rec->start, s);
-  if (launch_attend_planned(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (in.num_wide_groups > 0 && launch_attend_wide(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (in.num_wgs > 0 && launch_attend_planned(a, s) != hipSuccess) return PA_ERR_LAUNCH;
   if (rec) (void)hipEventRecord(rec->mid, s);
   const bool merge = in.num_merge_rows > 0;
   if (merge && launch_attend_planned_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;

@@ -133,9 +133,16 @@ struct PlanColumn {
 struct PlanMergeRow {
   int32_t q_row, j, e0, n;
 };
+// A wide group: up to kWideTiles items of one segment (the same sequence and
+// first block, other query columns) run by one workgroup per KV head, each
+// wave one item, every block read once into LDS for all of them.
+struct PlanWideGroup {
+  int32_t item0, nitems, blk_lo, blk_hi;
+};
+constexpr int kWideTiles = 8;
 
 struct PlanLayout {
-  size_t items_off, cols_off, rows_off, entries_off, wg_off, bytes;
+  size_t items_off, cols_off, rows_off, entries_off, wg_off, wide_off, bytes;
 };
 
 inline size_t align16(size_t n) { return (n + 15) / 16 * 16; }
@@ -147,7 +154,8 @@ inline PlanLayout plan_layout(const pa_plan_info& info) {
   l.rows_off = align16(l.cols_off + (size_t)info.num_columns * sizeof(PlanColumn));
   l.entries_off = align16(l.rows_off + (size_t)info.num_merge_rows * sizeof(PlanMergeRow));
   l.wg_off = align16(l.entries_off + (size_t)info.num_merge_entries * sizeof(int32_t));
-  l.bytes = align16(l.wg_off + (size_t)(info.num_wgs > 0 ? info.num_wgs + 1 : 0) * sizeof(int32_t));
+  l.wide_off = align16(l.wg_off + (size_t)(info.num_wgs > 0 ? info.num_wgs + 1 : 0) * sizeof(int32_t));
+  l.bytes = align16(l.wide_off + (size_t)info.num_wide_groups * sizeof(PlanWideGroup));
   return l;
 }
 
@@ -175,10 +183,12 @@ struct PlannedArgs {
   const PlanMergeRow* __restrict__ rows;
   const int32_t* __restrict__ entries;
   const int32_t* __restrict__ wg_start;
+  const PlanWideGroup* __restrict__ wide;
   float* ws_m;
   float* ws_l;
   float* ws_acc;
   int32_t num_items, num_columns, num_records, num_merge_rows, num_merge_entries, num_wgs, max_item_columns;
+  int32_t num_wide_groups;
   int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, num_blocks;
   int32_t waves_per_wg, head_groups;
@@ -188,6 +198,7 @@ struct PlannedArgs {
 
 hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream);
 hipError_t launch_attend_planned_merge(const PlannedArgs& a, hipStream_t stream);
+hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream);
 
 hipError_t launch_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -25,6 +25,11 @@
 // with sequences; every (run, slice) overlap is an item, and a workgroup
 // runs its slice's items in order.  No compute unit idles at the end of the
 // launch for lack of work.
+//
+// A segment with many tiles (a prefill chunk: hundreds of query columns
+// over the same blocks) would have each block read once per tile.  Its
+// tiles go to wide groups instead: up to 8 tiles, one workgroup per KV
+// head, one wave per tile, each block read once into LDS for the group.
 #include <algorithm>
 #include <cstring>
 #include <map>
@@ -39,6 +44,8 @@ constexpr int kBlockTokens = PA_BLOCK_SIZE;
 constexpr int kTileCols = 32;          // query columns per item (two 16-column MFMA tiles)
 constexpr int kTargetWaves = 2048;     // waves over the device, about 8 per compute unit
 constexpr int kMaxWavesPerWg = 8;      // one wave per KV head, at most 8 per workgroup
+constexpr int kWideMinTiles = 4;       // a segment with this many tiles goes to wide groups
+constexpr int kWideMinPiece = 8;       // blocks per piece of a cut wide group, at least
 
 struct Segment {
   int seq;                       // block-table row the blocks are read from
@@ -50,6 +57,7 @@ struct Segment {
 struct PlanBuild {
   std::vector<PlanItem> items;
   std::vector<int32_t> wg_start;       // [num_wgs + 1]: workgroup x runs items wg_start[x] .. wg_start[x+1]-1
+  std::vector<PlanWideGroup> wide;     // wide groups; their items follow the sliced ones
   std::vector<PlanColumn> cols;
   std::vector<PlanMergeRow> rows;
   std::vector<int32_t> entries;
@@ -142,22 +150,30 @@ int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_
     segs.push_back(std::move(s));
   }
 
-  // ---- tiles (up to kTileCols columns each) and their block runs
+  // ---- tiles (up to kTileCols columns each) and their block runs.  A
+  // segment of at least kWideMinTiles tiles (a prefill chunk) goes to wide
+  // groups, the others to the equal slices.
   struct Tile {
     int seg, col0, ncols, lo, hi, kv_len;
   };
-  std::vector<Tile> tiles;
+  std::vector<Tile> tiles, wtiles;
   int64_t total = 0;
   for (size_t si = 0; si < segs.size(); ++si) {
     const Segment& s = segs[si];
+    std::vector<Tile> st;
     for (size_t c0 = 0; c0 < s.cols.size(); c0 += kTileCols) {
       const int n = (int)std::min<size_t>(kTileCols, s.cols.size() - c0);
       int max_h = 0;
       for (int k = 0; k < n; ++k) max_h = std::max(max_h, (int)pb.cols[s.cols[c0 + k]].horizon);
       const int hi = std::min(s.hi, ceil_div(max_h, kBlockTokens));
       if (hi <= s.lo) continue;                      // no column of this tile sees these blocks
-      tiles.push_back(Tile{(int)si, (int)c0, n, s.lo, hi, max_h});
-      total += hi - s.lo;
+      st.push_back(Tile{(int)si, (int)c0, n, s.lo, hi, max_h});
+    }
+    if ((int)st.size() >= kWideMinTiles) {
+      wtiles.insert(wtiles.end(), st.begin(), st.end());
+    } else {
+      for (const Tile& t : st) total += t.hi - t.lo;
+      tiles.insert(tiles.end(), st.begin(), st.end());
     }
   }
   // ---- runs of units in work order.  A segment with one tile is one run; the
@@ -245,6 +261,66 @@ int build_plan(const int32_t* q_start, const int32_t* context_lens, const int32_
     pb.wg_start[ct.slice + 1] = (int32_t)pb.items.size();
   }
   for (int x = 1; x <= n; ++x) pb.wg_start[x] = std::max(pb.wg_start[x], pb.wg_start[x - 1]);
+
+  // ---- wide groups: up to kWideTiles consecutive tiles of one segment (the
+  // same first block); their runs are cut into pieces only when the groups
+  // times the KV heads would not give about kTargetWaves / kWideTiles
+  // workgroups, each piece at least kWideMinPiece blocks.  A tile's item is
+  // direct when its segment is its columns' only one and it is not cut.
+  std::vector<int32_t> wtile_col0(wtiles.size(), -1);
+  struct Group {
+    size_t t0, t1;
+    int lo, hi;
+  };
+  std::vector<Group> groups;
+  for (size_t t0 = 0; t0 < wtiles.size();) {
+    size_t t1 = t0;
+    int hi = wtiles[t0].lo;
+    while (t1 < wtiles.size() && wtiles[t1].seg == wtiles[t0].seg && t1 - t0 < (size_t)kWideTiles)
+      hi = std::max(hi, wtiles[t1++].hi);
+    groups.push_back(Group{t0, t1, wtiles[t0].lo, hi});
+    t0 = t1;
+  }
+  const int64_t have = (int64_t)groups.size() * num_kv_heads;
+  const int64_t want_wide = kTargetWaves / kWideTiles;
+  const int pieces = have > 0 && have < want_wide ? (int)((want_wide + have - 1) / have) : 1;
+  for (const Group& gr : groups) {
+    const int len = gr.hi - gr.lo;
+    const int np = std::max(1, std::min(pieces, len / kWideMinPiece));
+    for (int k = 0; k < np; ++k) {
+      const int plo = gr.lo + (int)((int64_t)k * len / np), phi = gr.lo + (int)((int64_t)(k + 1) * len / np);
+      PlanWideGroup wg{(int32_t)pb.items.size(), 0, plo, plo};
+      for (size_t t = gr.t0; t < gr.t1; ++t) {
+        const Tile& tl = wtiles[t];
+        const Segment& s = segs[tl.seg];
+        const int hi = std::min(phi, tl.hi);
+        if (hi <= plo) continue;                     // this tile's columns see none of the piece
+        if (wtile_col0[t] < 0) {
+          wtile_col0[t] = (int32_t)item_cols.size();
+          for (int c = 0; c < tl.ncols; ++c) item_cols.push_back(pb.cols[s.cols[tl.col0 + c]]);
+        }
+        const bool direct = !s.partial && np == 1;
+        PlanItem it{};
+        it.seq = s.seq;
+        it.blk_lo = plo;
+        it.blk_hi = hi;
+        it.col0 = wtile_col0[t];
+        it.ncols = tl.ncols;
+        it.kv_len = tl.kv_len;
+        it.rec0 = direct ? -1 : pb.records;
+        if (!direct) {
+          for (int c = 0; c < tl.ncols; ++c) col_recs[s.cols[tl.col0 + c]].push_back(pb.records + c);
+          pb.records += tl.ncols;
+        }
+        pb.items.push_back(it);
+        ++wg.nitems;
+        wg.blk_hi = std::max(wg.blk_hi, hi);
+      }
+      if (wg.nitems == 0) continue;
+      pb.block_reads += wg.blk_hi - wg.blk_lo;
+      pb.wide.push_back(wg);
+    }
+  }
   pb.cols = std::move(item_cols);
 
   // ---- merge rows: every column with partial records, in column order
@@ -291,6 +367,7 @@ PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_l
   info->num_merge_entries = (int32_t)pb.entries.size();
   info->num_shared_groups = pb.groups;
   info->num_wgs = pb.wg_start.empty() ? 0 : (int32_t)pb.wg_start.size() - 1;
+  info->num_wide_groups = (int32_t)pb.wide.size();
   for (const PlanItem& it : pb.items) info->max_item_columns = std::max(info->max_item_columns, it.ncols);
   const PlanLayout lay = plan_layout(*info);
   info->plan_bytes = (int64_t)lay.bytes;
@@ -307,5 +384,6 @@ PA_EXPORT int pa_plan_attention(const int32_t* q_start, const int32_t* context_l
     std::memcpy(p + lay.entries_off, pb.entries.data(), pb.entries.size() * sizeof(int32_t));
   if (!pb.wg_start.empty())
     std::memcpy(p + lay.wg_off, pb.wg_start.data(), pb.wg_start.size() * sizeof(int32_t));
+  if (!pb.wide.empty()) std::memcpy(p + lay.wide_off, pb.wide.data(), pb.wide.size() * sizeof(PlanWideGroup));
   return PA_OK;
 }

@@ -15,12 +15,13 @@ def _align16(n: int) -> int:
 
 
 def unpack_plan(plan: np.ndarray, info) -> dict:
-    """Structured views of the four arrays of a packed plan."""
+    """Structured views of the arrays of a packed plan."""
     items_off = 0
     cols_off = _align16(items_off + info.num_items * 32)
     rows_off = _align16(cols_off + info.num_columns * 16)
     ent_off = _align16(rows_off + info.num_merge_rows * 16)
     wg_off = _align16(ent_off + info.num_merge_entries * 4)
+    wide_off = _align16(wg_off + (info.num_wgs + 1 if info.num_wgs else 0) * 4)
     raw = plan.view(np.uint8)
 
     def view(off, n, width):
@@ -34,6 +35,8 @@ def unpack_plan(plan: np.ndarray, info) -> dict:
         "rows": view(rows_off, info.num_merge_rows, 4),
         "entries": raw[ent_off:ent_off + info.num_merge_entries * 4].view(np.int32),
         "wg_start": raw[wg_off:wg_off + (info.num_wgs + 1 if info.num_wgs else 0) * 4].view(np.int32),
+        # wide groups: (first item, items, first block, end block)
+        "wide": view(wide_off, info.num_wide_groups, 4),
     }
 
 

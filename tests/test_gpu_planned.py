@@ -83,6 +83,26 @@ def test_chunked_prefill_chunk():
     assert err <= TOL["bf16"]
 
 
+def test_prefill_chunk_bench_shape():
+    """The measured prefill chunk (4 sequences, 512 new tokens each at 4096
+    context, 8B shape): wide groups only, every item direct; two sequences
+    checked in full against the oracle."""
+    wl = W.make_multi_query_workload(name="chunk-bench", seed=303, context_lens=[4096] * 4, q_lens=[512] * 4,
+                                     num_q_heads=32, num_kv_heads=8, head_dim=128)
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    seqs = [0, 3]
+    want = oracle.multi_query_ref(wl.q, wl.q_start, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale,
+                                  "bf16", "bf16", seqs=seqs)
+    out, info = _run(dw, wl)
+    assert info.num_wide_groups == 32 and info.num_wgs == 0
+    rows = np.concatenate([np.arange(wl.q_start[b], wl.q_start[b + 1]) for b in seqs])
+    err = float(np.abs(out_to_f64(out)[rows] - want[rows]).max())
+    log(f"prefill chunk (bench shape): wide groups={info.num_wide_groups} max abs error {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_decode_through_a_plan_matches_oracle():
     wl = W.make_workload(name="plan-decode", seed=204, context_lens=[1, 17, 600, 1500, 33], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")

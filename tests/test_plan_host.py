@@ -75,16 +75,32 @@ def test_shared_prefix_plan_reads_prefix_once():
 
 
 def check_slices(plan, info):
-    """Workgroup x runs items wg_start[x] .. wg_start[x+1]-1; every item belongs
-    to exactly one workgroup and the workgroups' block counts differ by at most one."""
+    """Workgroup x runs items wg_start[x] .. wg_start[x+1]-1 and the wide groups
+    own the items after those; every item belongs to exactly one workgroup or
+    wide group, the slices' block counts differ by at most one, and a wide
+    group's items share sequence and first block, inside the group's run."""
     p = unpack_plan(plan, info)
-    ws, it = p["wg_start"], p["items"]
+    ws, it, wide = p["wg_start"], p["items"], p["wide"]
     if info.num_items == 0:
-        assert info.num_wgs == 0
+        assert info.num_wgs == 0 and info.num_wide_groups == 0
         return
-    assert ws[0] == 0 and ws[-1] == info.num_items and np.all(np.diff(ws) >= 1)
-    loads = [int((it["blk_hi"][ws[x]:ws[x + 1]] - it["blk_lo"][ws[x]:ws[x + 1]]).sum()) for x in range(info.num_wgs)]
-    assert max(loads) - min(loads) <= 1 and sum(loads) == info.block_reads
+    n_sliced = int(ws[-1]) if info.num_wgs else 0
+    reads = 0
+    if info.num_wgs:
+        assert ws[0] == 0 and np.all(np.diff(ws) >= 1)
+        loads = [int((it["blk_hi"][ws[x]:ws[x + 1]] - it["blk_lo"][ws[x]:ws[x + 1]]).sum())
+                 for x in range(info.num_wgs)]
+        assert max(loads) - min(loads) <= 1
+        reads += sum(loads)
+    nxt = n_sliced
+    for item0, n, lo, hi in wide:
+        assert item0 == nxt and 1 <= n <= 8 and lo < hi
+        sl = slice(item0, item0 + n)
+        assert np.all(it["seq"][sl] == it["seq"][item0]) and np.all(it["blk_lo"][sl] == lo)
+        assert np.all(it["blk_hi"][sl] <= hi) and it["blk_hi"][sl].max() == hi and np.all(it["ncols"][sl] <= 32)
+        reads += int(hi - lo)
+        nxt += n
+    assert nxt == info.num_items and reads == info.block_reads
 
 
 def test_default_slices_fill_the_device():
@@ -155,6 +171,76 @@ def test_shared_prefix_plan_executed_on_cpu_matches_oracle_decode():
     assert info.num_shared_groups == 2
     got = run_plan_cpu(plan, info, wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", "bf16")
     assert np.abs(got - want).max() < 1e-12
+
+
+def test_prefill_chunk_goes_to_wide_groups():
+    """4 chunks of 512 new tokens at 4096 context, group 4: 2048 columns = 64
+    tiles per sequence, 8 wide groups of 8 tiles each; 32 groups x 8 KV heads
+    fill the device, so no run is cut: every item writes its output directly
+    and each KV head reads each block once per group."""
+    ctxs, q_lens = [4096] * 4, [512] * 4
+    bt = _tables(ctxs, np.random.default_rng(11))
+    plan, info = pa.pa_plan_attention(np.array(ctxs), 32, 8, 128, q_start=_q_start(q_lens))
+    assert info.num_wide_groups == 32 and info.num_wgs == 0 and info.num_records == 0
+    assert info.num_items == 4 * 64 and info.max_item_columns == 32
+    check_slices(plan, info)
+    check_coverage(plan, info, _q_start(q_lens), ctxs, bt, 4)
+    # a group's run ends at its last tile's horizon: chunk tokens 64g .. 64g+63 see up to 3584 + 64(g+1)
+    wide = unpack_plan(plan, info)["wide"]
+    assert sorted(int(h) for h in wide[:8, 3]) == [(3584 + 64 * (k + 1)) // 16 for k in range(8)]
+    assert info.block_reads == 4 * sum(int(h) for h in wide[:8, 3])
+
+
+def test_short_prefill_wide_groups_are_cut_into_pieces():
+    """One 128-token chunk (512 columns, 2 groups): 2 groups x 8 heads are far
+    from filling the device, so each group's run is cut into pieces of at
+    least 8 blocks, with partial records merged per column."""
+    ctxs, q_lens = [1024], [128]
+    bt = _tables(ctxs, np.random.default_rng(12))
+    plan, info = pa.pa_plan_attention(np.array(ctxs), 32, 8, 128, q_start=_q_start(q_lens))
+    assert info.num_wgs == 0 and info.num_wide_groups > 2 and info.num_records > 0
+    wide = unpack_plan(plan, info)["wide"]
+    assert np.all(wide[:, 3] - wide[:, 2] >= 8)
+    check_slices(plan, info)
+    check_coverage(plan, info, _q_start(q_lens), ctxs, bt, 4)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_wide_plan_executed_on_cpu_matches_oracle(kv):
+    """A mix of wide groups (the 40- and 33-token chunks at group 4: 160 and
+    132 columns) and sliced items (decode tokens), cut and uncut, run on the
+    CPU item by item: equal to the oracle's direct result."""
+    wl = W.make_multi_query_workload(name="wide", seed=13, context_lens=[300, 7, 170, 16, 90],
+                                     q_lens=[40, 1, 33, 1, 2], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                     kv_dtype=kv)
+    if kv == "fp8":
+        wl.k_cache = oracle.quantize_pool_ref(wl.k_values, wl.k_scale)
+        wl.v_cache = oracle.quantize_pool_ref(wl.v_values, wl.v_scale)
+    k, v = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping, "bf16", kv,
+                                  wl.k_scale, wl.v_scale)
+    want = oracle.multi_query_ref(wl.q, wl.q_start, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
+                                  wl.k_scale, wl.v_scale)
+    for target in (0, 3):
+        plan, info = pa.pa_plan_attention(wl.context_lens, 8, 2, 64, q_start=wl.q_start, target_slices=target)
+        assert info.num_wide_groups >= 2 and info.num_wgs >= 1
+        check_slices(plan, info)
+        check_coverage(plan, info, wl.q_start, wl.context_lens, wl.block_tables, 4)
+        got = run_plan_cpu(plan, info, wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
+                           wl.k_scale, wl.v_scale)
+        assert np.abs(got - want).max() < 1e-12
+
+
+def test_many_samples_share_a_prefix_in_wide_groups():
+    """32 samples x 4 heads = 128 columns on one shared prefix: 4 tiles, one
+    wide group whose items leave records, merged with each sample's suffix."""
+    wl = W.make_shared_prefix_workload(name="share32", seed=14, num_prompts=1, samples_per_prompt=32,
+                                       prefix_tokens=96, suffix_max=40, num_q_heads=32, num_kv_heads=8,
+                                       head_dim=128, with_values=False)
+    ctx = wl.context_lens
+    plan, info = pa.pa_plan_attention(ctx, 32, 8, 128, block_tables=wl.block_tables_shared, share_prefix=True)
+    assert info.num_shared_groups == 1 and info.num_wide_groups >= 1 and info.num_records > 0
+    check_slices(plan, info)
+    check_coverage(plan, info, np.arange(len(ctx) + 1), ctx, wl.block_tables_shared, 4)
 
 
 def test_planner_rejects_bad_input():
