@@ -53,7 +53,7 @@ KERNELS = {
     "decode_8b_int4": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
     "shared_prefix_32x8": ("attend_planned_kernel", PLANNED_SOURCES),
     "verify4_8b": ("attend_planned_kernel", PLANNED_SOURCES),
-    "chunked_prefill": ("attend_planned_kernel", PLANNED_SOURCES),
+    "chunked_prefill": ("attend_wide_kernel", PLANNED_SOURCES),
     "serve_8b": ("decode_mfma_balanced_kernel", DECODE_SOURCES),
 }
 
@@ -369,7 +369,8 @@ def build_planned(args, pa, torch, np, W, oracle, name):
     return Bench(
         workload=label, steps=steps, pools=len(pools), step_bytes=kernel_bytes + write_bytes,
         kernel_bytes=kernel_bytes, kernel_flops=flops, num_seqs=wl.num_seqs, dtype="bf16",
-        kernel_label="planned attention kernel",
+        kernel_label=("planned attention kernels (wide groups %d, sliced workgroups %d)"
+                      % (info.num_wide_groups, info.num_wgs)),
         data="synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)", config=config,
         logical_bytes=logical_bytes, cpu_prepare=cpu_prepare, cpu_one=cpu_one,
         cpu_kind="decode_ref" if share else "multi_query_ref", mfma_bound=name == "chunked_prefill")
