@@ -307,8 +307,16 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
   extern __shared__ __align__(16) uint8_t s_wide[];          // 2 block buffers, then the waves' result stages
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, c = lane >> 4;
-  const int g = blockIdx.y;
-  const PlanWideGroup grp = a.wide[blockIdx.x];
+  // Workgroup b runs on XCD b mod 8.  Logical workgroup j = (KV head, group)
+  // in head-major order goes to XCD j / per_xcd, so the groups of one
+  // segment and head (consecutive j) share an XCD and its L2: they read the
+  // same blocks at about the same time, and the memory serves each once.
+  const int n = a.num_wide_groups * a.num_kv_heads;
+  const int per_xcd = (n + 7) / 8;
+  const int j = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (j >= n) return;                                        // (every wave of the workgroup)
+  const int g = j / a.num_wide_groups;
+  const PlanWideGroup grp = a.wide[j % a.num_wide_groups];
   const int nitems = clampi(grp.nitems, 0, kWideTiles);
   if (nitems == 0) return;                                   // (every wave of the workgroup)
   const int k0 = clampi(grp.item0, 0, a.num_items - 1);
@@ -504,7 +512,8 @@ size_t wide_lds_bytes() {
 }
 
 hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_wide_groups, a.num_kv_heads);
+  const int n = a.num_wide_groups * a.num_kv_heads;
+  const dim3 grid((n + 7) / 8 * 8);           // XCD-ordered (attend_wide_kernel); extra workgroups exit
   const dim3 block(64 * kWideTiles);
   const int f = a.cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (a.cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
 #define PA_LAUNCH(D_, F_) \

@@ -408,10 +408,10 @@ struct HeadState {
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
     l += (p[0] + p[1]) + (p[2] + p[3]);
-    // e4m3: the block's V scale is applied in fp32 to the block's P.V product
-    // (folding it into the bf16 P would put a relative 2^-9 error on every V row)
-    const float pv = T::kScaled ? 1.0f : vs;
-    const uint2 pbits = make_uint2(pack_bf16x2(p[0] * pv, p[1] * pv), pack_bf16x2(p[2] * pv, p[3] * pv));
+    // e4m3/int4: the block's V scale is applied in fp32 to the block's P.V
+    // product (folding it into the bf16 P would put a relative 2^-9 error on
+    // every V row); a bf16 cache has no V scale (callers pass vs = 1)
+    const uint2 pbits = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
     const short4_t pop = __builtin_bit_cast(short4_t, pbits);
     if constexpr (kInt4) {
       // the P.V MFMA sees V + 136: keep V scale * (sum of the bf16 P it used) to take off at the end
