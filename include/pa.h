@@ -343,6 +343,29 @@ int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * pa_upload — move a step's small host arrays (block tables, lengths,
+ * copy pairs) to the device on the compute stream.
+ *
+ * The continuous-batching step of "17 · 连续批处理与 PagedAttention"
+ * (section 二: the batch is re-formed every iteration) sends its freshly
+ * built block tables to the device before every decode step.  An ordinary
+ * asynchronous copy goes through a DMA engine, and the compute stream then
+ * waits on it and the DMA engine on the compute stream: tens of
+ * microseconds of idle GPU per iteration at the decode's scale.  pa_upload
+ * instead runs a copy kernel on `stream` that reads the pinned host buffer
+ * directly.
+ *
+ * src: page-locked host memory mapped for the device (hipHostMalloc, or a
+ * pinned torch tensor); dst: device memory; both 16-byte aligned; bytes a
+ * multiple of 16.  The host must not change src until the kernel has run
+ * (record an event after the call).  Errors: NULL_POINTER, BAD_SHAPE
+ * (bytes not a multiple of 16), MISALIGNED, UNSUPPORTED (src is not
+ * device-mapped host memory, or dst is not device memory), LAUNCH.
+ * bytes == 0 is a no-op.
+ */
+int pa_upload(void* dst, const void* src, size_t bytes, void* stream);
+
+/*
  * Host block manager and the continuous-batching step (host memory only).
  *
  * A global pool of num_blocks physical blocks of 16 tokens, one block table

@@ -8,7 +8,7 @@ from ._lib import (BLOCK_SIZE, EXPORTED, HostBlockManager, LIB_PATH, OutOfBlocks
                    pa_cache_write, pa_cache_write_autoscale, pa_copy_blocks, pa_decode, pa_decode_append,
                    pa_decode_partition_tokens, pa_decode_workspace_size, pa_plan_attention, pa_probe_copy,
                    pa_probe_sink_bytes, pa_probe_stream_read, pa_status_string, pa_timing_enable, pa_timing_read,
-                   plan_to_device, prepare_attend_planned, prepare_cache_write, prepare_decode,
+                   pa_upload, plan_to_device, prepare_attend_planned, prepare_cache_write, prepare_decode,
                    prepare_decode_append)
 
 __all__ = [
@@ -17,5 +17,5 @@ __all__ = [
     "pa_cache_write", "pa_cache_write_autoscale", "pa_copy_blocks", "pa_decode", "pa_decode_append",
     "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_plan_attention", "pa_probe_copy",
     "pa_probe_sink_bytes", "pa_probe_stream_read", "pa_status_string", "pa_timing_enable", "pa_timing_read",
-    "plan_to_device", "prepare_attend_planned", "prepare_cache_write", "prepare_decode", "prepare_decode_append",
+    "pa_upload", "plan_to_device", "prepare_attend_planned", "prepare_cache_write", "prepare_decode", "prepare_decode_append",
 ]

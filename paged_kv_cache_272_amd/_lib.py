@@ -71,6 +71,7 @@ _SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "pa_upload": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
@@ -270,6 +271,18 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: to
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), code, _ptr(k_scale),
                                _ptr(v_scale), _ptr(block_pairs), block_pairs.shape[0], hkv, d, num_blocks,
                                _stream(stream)), "pa_copy_blocks")
+
+
+def pa_upload(dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None, stream=None) -> None:
+    """Copy the first ``nbytes`` (default: all of ``src``) of a pinned host
+    tensor into a device tensor with a kernel on ``stream``.  Both contiguous,
+    16-byte aligned, ``nbytes`` a multiple of 16."""
+    if src.is_cuda or not src.is_contiguous():
+        raise ValueError("pa_upload: src must be a contiguous host tensor")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size() or n > dst.numel() * dst.element_size():
+        raise ValueError("pa_upload: nbytes exceeds a buffer")
+    _check(_lib.pa_upload(_ptr(dst), src.data_ptr(), n, _stream(stream)), "pa_upload")
 
 
 def _host_i32(a, name: str) -> Optional[np.ndarray]:

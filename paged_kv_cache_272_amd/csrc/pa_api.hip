@@ -351,6 +351,31 @@ PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype,
   return launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+PA_EXPORT int pa_upload(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!dst || !src) return PA_ERR_NULL_POINTER;
+  if (bytes % 16) return PA_ERR_BAD_SHAPE;
+  if (!aligned16(dst) || !aligned16(src)) return PA_ERR_MISALIGNED;
+  // the kernel reads src through its device mapping: only page-locked,
+  // device-mapped host memory qualifies, and dst must be device memory
+  hipPointerAttribute_t sa{}, da{};
+  if (hipPointerGetAttributes(&sa, src) != hipSuccess) {
+    (void)hipGetLastError();                      // pageable memory: clear the query's error
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (sa.type != hipMemoryTypeHost || !sa.devicePointer || !sa.hostPointer) return PA_ERR_UNSUPPORTED;
+  if (hipPointerGetAttributes(&da, dst) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (da.type != hipMemoryTypeDevice) return PA_ERR_UNSUPPORTED;
+  // the device address of src itself (the mapping's device pointer shifted by src's offset from its host pointer)
+  const char* dev_src = static_cast<const char*>(sa.devicePointer) +
+                        (static_cast<const char*>(src) - static_cast<const char*>(sa.hostPointer));
+  return launch_upload(dst, dev_src, bytes, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                                 : PA_ERR_LAUNCH;
+}
+
 PA_EXPORT int pa_attend_planned(void* out, const void* q, pa_dtype q_dtype, const void* k_cache,
                                 const void* v_cache, pa_dtype cache_dtype, const float* k_scale,
                                 const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -202,6 +202,7 @@ hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream);
 
 hipError_t launch_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);
 size_t probe_sink_bytes();
 
 }  // namespace pa

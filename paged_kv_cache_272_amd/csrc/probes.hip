@@ -1,6 +1,7 @@
 // Measurement probes: a plain 16-byte streaming read and a plain copy.
 // They give the bandwidth the memory system sustains for a simple stream,
-// the ceiling the decode kernels are compared with.
+// the ceiling the decode kernels are compared with.  And the upload copy
+// (pa_upload): the same loop reading device-mapped host memory.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -37,7 +38,24 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(uint4* dst, c
   for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Upload: a grid-stride 16-byte copy from device-mapped host memory.
+constexpr int kUploadThreads = 256;
+
+__global__ __launch_bounds__(kUploadThreads) void upload_kernel(uint4* dst, const uint4* src, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kUploadThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kUploadThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t want = (n16 + kUploadThreads - 1) / kUploadThreads;
+  const int grid = (int)(want < 64 ? (want < 1 ? 1 : want) : 64);     // a few workgroups: the reads cross PCIe
+  hipLaunchKernelGGL(upload_kernel, dim3(grid), dim3(kUploadThreads), 0, stream, reinterpret_cast<uint4*>(dst),
+                     reinterpret_cast<const uint4*>(src), n16);
+  return hipGetLastError();
+}
 
 size_t probe_sink_bytes() { return (size_t)kProbeBlocks * 16; }
 

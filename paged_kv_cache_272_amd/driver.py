@@ -2,8 +2,9 @@
 
 The native host block manager (pa_bm_*) decides every iteration's slots,
 copy-on-write pairs and block tables; this class moves those small host
-arrays to the device and issues the library's kernels in order:
-pa_copy_blocks for the pairs (if any), then pa_decode_append (the newest
+arrays to the device in one pa_upload (a copy kernel on the compute stream)
+and issues the library's kernels in order: pa_copy_blocks for the pairs
+(if any), then pa_decode_append (the newest
 token's K/V written into its slot and attended over).  This is the
 per-iteration scheduling of "17 · 连续批处理与 PagedAttention" section 二 (the
 batch is re-formed after every token; finished sequences leave and waiting
@@ -37,25 +38,37 @@ class DecodeDriver:
         self.device = torch.device(device)
         self.k_cache = torch.empty(num_blocks, num_kv_heads, BLOCK_SIZE, head_dim, dtype=dtype, device=self.device)
         self.v_cache = torch.empty_like(self.k_cache)
-        # two sets of pinned host buffers, used in turn; a set is refilled only
-        # after the copies that read it have finished
+        # The per-iteration arrays share one buffer, [lens | pairs | tables],
+        # each section starting on 16 bytes, so that one pa_upload moves the
+        # used prefix to the device copy of the same layout.  Two pinned host
+        # buffers are used in turn; a buffer is refilled only after the
+        # upload that read it has finished.
+        r16 = lambda n: (n + 3) // 4 * 4  # int32 elements to a multiple of 16 bytes
+        self._off_pr = r16(max_batch)
+        self._off_bt = self._off_pr + r16(2 * max_batch)
+        self._words = self._off_bt + r16(max_batch * max_blocks_per_seq)
         self._host = []
         for _ in range(2):
+            buf = torch.zeros(self._words, dtype=torch.int32).pin_memory()
             self._host.append({
-                "bt": torch.zeros(max_batch, max_blocks_per_seq, dtype=torch.int32).pin_memory(),
-                "cl": torch.zeros(max_batch, dtype=torch.int32).pin_memory(),
+                "buf": buf,
+                "views": self._views(buf),
                 "sl": torch.zeros(max_batch, dtype=torch.int64).pin_memory(),
-                "pr": torch.zeros(max_batch, 2, dtype=torch.int32).pin_memory(),
                 "done": None,
             })
         self._turn = 0
-        self.bt = torch.zeros(max_batch, max_blocks_per_seq, dtype=torch.int32, device=self.device)
-        self.cl = torch.zeros(max_batch, dtype=torch.int32, device=self.device)
-        self.pr = torch.zeros(max_batch, 2, dtype=torch.int32, device=self.device)
+        self._dev = torch.zeros(self._words, dtype=torch.int32, device=self.device)
+        self.cl, self.pr, self.bt = self._views(self._dev)
         ws = _lib.pa_decode_workspace_size(max_batch, num_q_heads, num_kv_heads, head_dim,
                                            max_blocks_per_seq * BLOCK_SIZE, 0)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
         self.last_pairs = 0
+
+    def _views(self, buf: torch.Tensor):
+        """(lens [max_batch], pairs [max_batch, 2], tables [max_batch, mb]) over a packed buffer."""
+        n, mb = self.max_batch, self.mb
+        return (buf[:n], buf[self._off_pr:self._off_pr + 2 * n].view(n, 2),
+                buf[self._off_bt:self._off_bt + n * mb].view(n, mb))
 
     # -- sequences
     def add_sequence(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> None:
@@ -92,13 +105,10 @@ class DecodeDriver:
         self._turn ^= 1
         if h["done"] is not None:
             h["done"].synchronize()
-        bt, cl, _, pr = self.bm.step(seqs, self.mb, out=(h["bt"].numpy(), h["cl"].numpy(), h["sl"].numpy(),
-                                                        h["pr"].numpy()))
+        hcl, hpr, hbt = h["views"]
+        bt, cl, _, pr = self.bm.step(seqs, self.mb, out=(hbt.numpy(), hcl.numpy(), h["sl"].numpy(), hpr.numpy()))
         npairs = len(pr)
-        self.bt[:b].copy_(h["bt"][:b], non_blocking=True)
-        self.cl[:b].copy_(h["cl"][:b], non_blocking=True)
-        if npairs:
-            self.pr[:npairs].copy_(h["pr"][:npairs], non_blocking=True)
+        _lib.pa_upload(self._dev, h["buf"], (self._off_bt + (b * self.mb + 3) // 4 * 4) * 4)
         ev = torch.cuda.Event()
         ev.record()
         h["done"] = ev

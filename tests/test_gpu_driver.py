@@ -101,3 +101,34 @@ def test_driver_matches_oracle_shadow():
                 drv.finish(s)
     log(f"driver: {next_id} sequences admitted, {forks} forks, {preempted} preemptions")
     assert forks > 0 and preempted > 0
+
+
+@pytest.mark.parametrize("nbytes,offset", [(16, 0), (4096, 16), (98304, 48), (1 << 20, 0), (3 * (1 << 20) + 16, 32)])
+def test_upload_copies_pinned_bytes(nbytes, offset):
+    """pa_upload: bit copy of a pinned host range (also one starting inside
+    its allocation) into device memory, sizes across one and many grid sweeps;
+    the bytes after the range stay untouched."""
+    log(f"upload {nbytes} B at host offset {offset}")
+    rng = np.random.default_rng(nbytes + offset)
+    host = torch.from_numpy(rng.integers(0, 256, nbytes + offset + 64, dtype=np.uint8)).pin_memory()
+    src = host[offset:offset + nbytes]
+    dst = torch.full((nbytes + 64,), 7, dtype=torch.uint8, device="cuda")
+    pa.pa_upload(dst, src)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:nbytes], src.numpy())
+    assert (got[nbytes:] == 7).all()
+
+
+def test_upload_rejects_unpinned_and_odd_sizes():
+    dst = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    plain = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_upload(dst, plain)
+    assert e.value.status == -4  # PA_ERR_UNSUPPORTED
+    pinned = torch.zeros(64, dtype=torch.uint8).pin_memory()
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_upload(dst, pinned, 24)
+    assert e.value.status == -2  # PA_ERR_BAD_SHAPE
+    torch.cuda.synchronize()
+    assert (dst.cpu().numpy() == 0).all()
