@@ -286,7 +286,7 @@ typedef struct pa_plan_info {
   int32_t num_shared_groups;  /* runs of prefix blocks read once for several sequences */
   int32_t num_wgs;            /* workgroups (equal slices of the work) per KV-head group */
   int32_t max_item_columns;   /* most query columns of one item (<= 32) */
-  int32_t num_wide_groups;    /* groups of up to 8 items of one long segment sharing each block (see below) */
+  int32_t num_wide_groups;    /* groups of up to 4 items of one long segment sharing each block (see below) */
   int64_t plan_bytes;         /* size of the packed plan */
   int64_t workspace_bytes;    /* scratch pa_attend_planned needs (0: none) */
   int64_t block_reads;        /* blocks read per KV head (a wide group reads a block once for its items) */
@@ -305,7 +305,7 @@ typedef struct pa_plan_info {
  * (workgroups) to cut the work into (0 = automatic: about 2048 waves over
  * the device; never more slices than 16-token blocks to read).  A
  * segment with many query columns (a chunked-prefill chunk: q_len x group
- * columns, at least 4 tiles of 32) goes to wide groups instead: up to 8 of
+ * columns, at least 4 tiles of 32) goes to wide groups instead: up to 4 of
  * its 32-column items, one workgroup per KV head, every block read once
  * into LDS for all of them; their block runs are split into pieces only
  * when the groups alone would not fill the device.  `plan` receives

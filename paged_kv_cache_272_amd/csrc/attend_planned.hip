@@ -273,10 +273,13 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
 // the group (up to two 16-column tiles).  The group's items share their
 // sequence and first block, so every block of the group's run is read from
 // memory once, by the whole workgroup, into LDS, and each wave folds it into
-// its own tiles from there: the 8 tiles of a prefill chunk cost one read of
-// each block instead of eight.  Blocks alternate between two LDS buffers:
-// block i+1 is loaded into registers while block i is folded in, then
-// written to the other buffer before the barrier that ends the step.
+// its own tiles from there: the 4 items of a prefill chunk cost one read of
+// each block instead of four.  Blocks alternate between two LDS buffers:
+// block i+1 is written to one while block i is folded in from the other.
+// Two workgroups share a CU.
+
+constexpr int kWideBufs = 2;
+constexpr int kWideAhead = 4;   // blocks in flight per thread (6 and 8 measured no faster)
 
 template <int D, int kFmt>
 struct WideLayout {
@@ -286,7 +289,8 @@ struct WideLayout {
   static constexpr int kBuf = 2 * kHalf;                               // K then V
   static constexpr int kPiecesPerRow = kRowBytes / 16;
   static constexpr int kPieces = 2 * kBlockTokens * kPiecesPerRow;     // 16-byte pieces per block, K and V
-  static_assert(kPieces <= 64 * kWideTiles, "one piece per thread");
+  static constexpr int kThreads = 64 * kWideTiles;
+  static constexpr int kPiecesPerThread = (kPieces + kThreads - 1) / kThreads;
 };
 
 // The register layout of load_block, read from a block staged in LDS.
@@ -301,10 +305,10 @@ __device__ __forceinline__ void load_block_lds(BlockRegs<D, kFmt>& br, const uin
 }
 
 template <int D, int kFmt>
-__global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArgs a) {
+__global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(PlannedArgs a) {   // two workgroups per CU
   constexpr int kTiles = 2;
   using L = WideLayout<D, kFmt>;
-  extern __shared__ __align__(16) uint8_t s_wide[];          // 2 block buffers, then the waves' result stages
+  extern __shared__ __align__(16) uint8_t s_wide[];          // kWideBufs block buffers, then the waves' result stages
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, c = lane >> 4;
   // Workgroup b runs on XCD b mod 8.  Logical workgroup j = (KV head, group)
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
   const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
-  float* stage = reinterpret_cast<float*>(s_wide + 2 * L::kBuf) + wave * kStageRows * D;
+  float* stage = reinterpret_cast<float*>(s_wide + kWideBufs * L::kBuf) + wave * kStageRows * D;
 
   // this wave's columns and query rows
   PlanColumn cols[kTiles];
@@ -364,22 +368,45 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
   };
   load_ids();
 
-  // This thread's 16-byte piece of a block: K rows first, then V rows.
-  // Threads past the pieces load piece 0 and drop it, so every wave issues
-  // one load per block.
-  const bool loader = tid < L::kPieces;
-  const int half = loader && tid >= L::kPieces / 2 ? 1 : 0;
-  const int pidx = loader ? tid - half * (L::kPieces / 2) : 0;
-  const int prow = pidx / L::kPiecesPerRow, pcol = pidx % L::kPiecesPerRow;
-  const int lds_off = half * L::kHalf + prow * L::kStride + pcol * 16;
+  // This thread's 16-byte pieces of a block (piece tid + k * threads): K
+  // rows first, then V rows.  Threads past the pieces load piece 0 and drop
+  // it, so every wave issues the same loads per block.
+  constexpr int kPP = L::kPiecesPerThread;
+  bool loader[kPP];
+  int64_t src_off[kPP];   // byte offset of the piece in a block's K (or V) rows of one head
+  int lds_off[kPP];
+  bool is_v[kPP];
+#pragma unroll
+  for (int k = 0; k < kPP; ++k) {
+    const int piece = tid + k * L::kThreads;
+    loader[k] = piece < L::kPieces;
+    const int half = loader[k] && piece >= L::kPieces / 2 ? 1 : 0;
+    const int pidx = loader[k] ? piece - half * (L::kPieces / 2) : 0;
+    const int prow = pidx / L::kPiecesPerRow, pcol = pidx % L::kPiecesPerRow;
+    is_v[k] = half != 0;
+    src_off[k] = (int64_t)prow * L::kRowBytes + pcol * 16;
+    lds_off[k] = half * L::kHalf + prow * L::kStride + pcol * 16;
+  }
+  struct Pieces {
+    uint4 v[kPP];
+  };
   auto load_piece = [&](int i) {
     if (i - idbase >= 64) {
       idbase += 64;
       load_ids();
     }
     const int64_t blk = __builtin_amdgcn_readlane(my_blk, i - idbase);
-    const int64_t head_row0 = (blk * a.num_kv_heads + g) * kBlockTokens;
-    return *reinterpret_cast<const uint4*>((half ? vbase : kbase) + (head_row0 + prow) * L::kRowBytes + pcol * 16);
+    const int64_t head0 = (blk * a.num_kv_heads + g) * kBlockTokens * L::kRowBytes;
+    Pieces pc;
+#pragma unroll
+    for (int k = 0; k < kPP; ++k)
+      pc.v[k] = *reinterpret_cast<const uint4*>((is_v[k] ? vbase : kbase) + head0 + src_off[k]);
+    return pc;
+  };
+  auto store_pieces = [&](uint8_t* buf, const Pieces& pc) {
+#pragma unroll
+    for (int k = 0; k < kPP; ++k)
+      if (loader[k]) *reinterpret_cast<uint4*>(buf + lds_off[k]) = pc.v[k];
   };
   auto lds_barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(0xc07f);      // this wave's LDS writes and reads are done (lgkmcnt(0))
@@ -392,12 +419,13 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
   // other buffer.  Every step issues exactly one load (past the run's end a
   // copy of its last block) so the waits before the writes leave the later
   // loads in flight.
-  constexpr int kAhead = 4;
+  constexpr int kAhead = kWideAhead;
+  auto buf = [&](int i) { return s_wide + ((i - lo) & 1) * L::kBuf; };
   if (lo < hi) {
-    uint4 ring[kAhead];
+    Pieces ring[kAhead];
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) ring[k] = load_piece(min(lo + k, hi - 1));
-    if (loader) *reinterpret_cast<uint4*>(s_wide + lds_off) = ring[0];
+    store_pieces(buf(lo), ring[0]);
     lds_barrier();
     for (int i0 = lo; i0 < hi; i0 += kAhead) {
 #pragma unroll
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
         ring[k] = load_piece(min(i + kAhead, hi - 1));
         if (i < hi && has_item && i < it_hi) {
           BlockRegs<D, kFmt> br;
-          load_block_lds<D, kFmt>(br, s_wide + ((i - lo) & 1) * L::kBuf, r, c);
+          load_block_lds<D, kFmt>(br, buf(i), r, c);
           float ks = 1.0f, vs = 1.0f;
           if constexpr (kFmt != kFmtBf16) {
             ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i - idbase));
@@ -415,11 +443,12 @@ __global__ __launch_bounds__(64 * kWideTiles) void attend_wide_kernel(PlannedArg
           const int t0 = i * kBlockTokens;
           const int valid = min(kBlockTokens, it.kv_len - t0);
           const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(br, valid, c);
-          hs[0].step_cols(br, vo, valid, horizon[0] - t0, a.scale_log2 * ks, vs, c);
-          if (second) hs[1].step_cols(br, vo, valid, horizon[1] - t0, a.scale_log2 * ks, vs, c);
+          if (second)
+            step_cols2(hs[0], hs[1], br, vo, valid, horizon[0] - t0, horizon[1] - t0, a.scale_log2 * ks, vs, c);
+          else
+            hs[0].step_cols(br, vo, valid, horizon[0] - t0, a.scale_log2 * ks, vs, c);
         }
-        if (i + 1 < hi && loader)
-          *reinterpret_cast<uint4*>(s_wide + ((i + 1 - lo) & 1) * L::kBuf + lds_off) = ring[(k + 1) % kAhead];
+        if (i + 1 < hi) store_pieces(buf(i + 1), ring[(k + 1) % kAhead]);
         lds_barrier();
       }
     }
@@ -508,7 +537,7 @@ hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
 // LDS of a wide workgroup: two block buffers, then a result stage per wave.
 template <int D, int kFmt>
 size_t wide_lds_bytes() {
-  return 2 * (size_t)WideLayout<D, kFmt>::kBuf + (size_t)kWideTiles * kStageRows * D * sizeof(float);
+  return kWideBufs * (size_t)WideLayout<D, kFmt>::kBuf + (size_t)kWideTiles * kStageRows * D * sizeof(float);
 }
 
 hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream) {

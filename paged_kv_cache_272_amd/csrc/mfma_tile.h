@@ -92,16 +92,31 @@ struct Tile {
 // the true one plus 136 times the sum of the other operand.
 constexpr float kInt4Bias = 136.0f;
 
+// Byte selectors of v_perm_b32 (__builtin_amdgcn_perm(src0, src1, sel)):
+// output byte k takes byte sel[k] of the 8-byte value src0:src1 (0-3 from
+// src1, 4-7 from src0).
+__device__ __forceinline__ constexpr uint32_t perm_sel(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Two int4 codes in bytes k0, k1 of x (values 0..15) -> one word of bf16
+// bits 0x43cc (128 + code) for each: the high bytes come from a register
+// holding 0x43 in every byte.
+__device__ __forceinline__ uint32_t int4_pair_to_bf16x2(uint32_t x, uint32_t k0, uint32_t k1) {
+  return __builtin_amdgcn_perm(0x43434343u, x, perm_sel(k0, 4, k1, 4));
+}
+
 // 8 int4 codes (one word, element 2i in the low nibble of byte i) -> 4 words
 // of bf16 pairs (elements 2i, 2i+1 in word i).
 __device__ __forceinline__ void int4x8_to_bf16x8(uint32_t w, uint32_t* out) {
   const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // byte i of lo -> bits 0-7, byte i of hi -> bits 16-23, zeros elsewhere
-    const uint32_t sel = (uint32_t)i | 0x0c00u | ((uint32_t)(4 + i) << 16) | 0x0c000000u;
-    out[i] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
-  }
+  // elements 0-3 and 4-7 in order, one code per byte
+  const uint32_t x01 = __builtin_amdgcn_perm(hi, lo, perm_sel(0, 4, 1, 5));
+  const uint32_t x23 = __builtin_amdgcn_perm(hi, lo, perm_sel(2, 6, 3, 7));
+  out[0] = int4_pair_to_bf16x2(x01, 0, 1);
+  out[1] = int4_pair_to_bf16x2(x01, 2, 3);
+  out[2] = int4_pair_to_bf16x2(x23, 0, 1);
+  out[3] = int4_pair_to_bf16x2(x23, 2, 3);
 }
 
 // Load `W` 32-bit words from a 4*W-byte aligned address.
@@ -226,19 +241,35 @@ __device__ __forceinline__ VOperands<D, kFmt> make_voperands(const BlockRegs<D, 
       for (int w = 0; w < T::kVWords; ++w) vw[e][w] = br.v[e][w];
   }
   VOperands<D, kFmt> vo;
+  if constexpr (kFmt == kFmtInt4) {
+    // nibble nn of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code.
+    // Even nn are low nibbles, odd nn high ones.  x[h][k]: codes of bytes
+    // 2k', 2k'+1 (k' = k mod 2) interleaved over tokens 0, 1 (k < 2) or 2, 3.
+    uint32_t x[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t n4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n4[e] = (h ? vw[e][0] >> 4 : vw[e][0]) & 0x0f0f0f0fu;
+      x[h][0] = __builtin_amdgcn_perm(n4[1], n4[0], perm_sel(0, 4, 1, 5));
+      x[h][1] = __builtin_amdgcn_perm(n4[1], n4[0], perm_sel(2, 6, 3, 7));
+      x[h][2] = __builtin_amdgcn_perm(n4[3], n4[2], perm_sel(0, 4, 1, 5));
+      x[h][3] = __builtin_amdgcn_perm(n4[3], n4[2], perm_sel(2, 6, 3, 7));
+    }
+#pragma unroll
+    for (int nn = 0; nn < T::kE; ++nn) {
+      const int h = nn & 1, byte = nn / 2;          // code byte `byte` of each token's word
+      const int k = byte / 2, b = 2 * (byte % 2);   // its interleaved word and position there
+      const uint32_t lo = int4_pair_to_bf16x2(x[h][k], b, b + 1);
+      const uint32_t hi = int4_pair_to_bf16x2(x[h][k + 2], b, b + 1);
+      vo.v[nn] = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+    }
+    return vo;
+  }
 #pragma unroll
   for (int nn = 0; nn < T::kE; ++nn) {
     uint32_t lo, hi;
-    if constexpr (kFmt == kFmtInt4) {
-      // nibble nn of each of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code
-      const uint32_t sel = (uint32_t)(nn / 2) | 0x0c00u | ((uint32_t)(4 + nn / 2) << 16) | 0x0c000000u;
-      const uint32_t b01 = __builtin_amdgcn_perm(vw[1][0], vw[0][0], sel);
-      const uint32_t b23 = __builtin_amdgcn_perm(vw[3][0], vw[2][0], sel);
-      lo = ((nn & 1) ? (b01 >> 4) : b01) & 0x000f000fu;
-      hi = ((nn & 1) ? (b23 >> 4) : b23) & 0x000f000fu;
-      lo |= 0x43004300u;
-      hi |= 0x43004300u;
-    } else if constexpr (kFmt == kFmtFp8) {
+    if constexpr (kFmt == kFmtFp8) {
       // byte nn%4 of word nn/4 from each of the 4 tokens -> [t0 t1 | t2 t3] codes -> bf16 pairs
       const int w = nn / 4, byte = nn % 4;
       const uint32_t sel = (uint32_t)byte | ((uint32_t)(byte + 4) << 8) | 0x0c0c0000u;
@@ -350,21 +381,41 @@ struct HeadState {
     // ---- S^T = K . Q^T
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int st = 0; st < T::kKSteps; ++st) {
-      uint4 kw;
-      if constexpr (kFmt == kFmtFp8) {
-        kw = make_uint4(fp8x2_to_bf16x2(br.k[2 * st], false), fp8x2_to_bf16x2(br.k[2 * st], true),
-                        fp8x2_to_bf16x2(br.k[2 * st + 1], false), fp8x2_to_bf16x2(br.k[2 * st + 1], true));
-      } else if constexpr (kInt4) {
-        uint32_t w4[4];
-        int4x8_to_bf16x8(br.k[st], w4);
-        kw = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      } else {
-        kw = make_uint4(br.k[4 * st], br.k[4 * st + 1], br.k[4 * st + 2], br.k[4 * st + 3]);
-      }
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qop[st], s, 0, 0, 0);
+    for (int st = 0; st < T::kKSteps; ++st)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(br, st), qop[st], s, 0, 0, 0);
+    float sv[4];
+    logits(s, sc, sv);
+    if (valid < kBlockTokens) hide_tokens(sv, valid, c);
+    if constexpr (kCols) {
+      // (a block every column sees in full needs no mask: wave-uniform test)
+      if (__ballot(col_valid < kBlockTokens) != 0) hide_tokens(sv, col_valid, c);
     }
-    // int4: the MFMA saw values + 136; remove 136 * (query sum) before scaling
+    // ---- online softmax (base 2)
+    raise_max<kCols>(fmaxf(m, block_max(sv)));
+    const short4_t pop = probs<kCols>(sv, vs);
+    pv(vo, pop, vs);
+  }
+
+  // The K operand of QK MFMA step st (K rows as bf16 pairs), the same for
+  // every tile that folds the block in.
+  static __device__ __forceinline__ bf16x8_t k_operand(const BlockRegs<D, kFmt>& br, int st) {
+    uint4 kw;
+    if constexpr (kFmt == kFmtFp8) {
+      kw = make_uint4(fp8x2_to_bf16x2(br.k[2 * st], false), fp8x2_to_bf16x2(br.k[2 * st], true),
+                      fp8x2_to_bf16x2(br.k[2 * st + 1], false), fp8x2_to_bf16x2(br.k[2 * st + 1], true));
+    } else if constexpr (kInt4) {
+      uint32_t w4[4];
+      int4x8_to_bf16x8(br.k[st], w4);
+      kw = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    } else {
+      kw = make_uint4(br.k[4 * st], br.k[4 * st + 1], br.k[4 * st + 2], br.k[4 * st + 3]);
+    }
+    return __builtin_bit_cast(bf16x8_t, kw);
+  }
+
+  // Base-2 logits of this lane's 4 scores: times sc (int4: less 136 times
+  // the query sum, the bias the MFMA saw).
+  __device__ __forceinline__ void logits(const f32x4_t& s, float sc, float* sv) {
     if constexpr (kInt4) {
       if (qbias_pending) {
         set_qbias();
@@ -372,26 +423,27 @@ struct HeadState {
       }
     }
     const float sb = -qbias * sc;
-    float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = kInt4 ? __builtin_fmaf(s[j], sc, sb) : s[j] * sc;
-    if (valid < kBlockTokens) {
+  }
+
+  // Remove the block's tokens from `limit` on (this lane's tokens 4c..4c+3).
+  static __device__ __forceinline__ void hide_tokens(float* sv, int limit, int c) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * c + j >= valid) sv[j] = -INFINITY;
-    }
-    if constexpr (kCols) {
-      // (a block every column sees in full needs no mask: wave-uniform test)
-      if (__ballot(col_valid < kBlockTokens) != 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * c + j >= col_valid) sv[j] = -INFINITY;
-      }
-    }
-    // ---- online softmax (base 2)
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = max_xor16(max_xor32(mx));
-    const float m_new = fmaxf(m, mx);
+    for (int j = 0; j < 4; ++j)
+      if (4 * c + j >= limit) sv[j] = -INFINITY;
+  }
+
+  // The block's max logit of this lane's column (over the 4 lane groups).
+  static __device__ __forceinline__ float block_max(const float* sv) {
+    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    return max_xor16(max_xor32(mx));
+  }
+
+  // Move the running max to m_new (>= m), rescaling l and acc, if any
+  // column's max grew (wave-uniform test).
+  template <bool kCols>
+  __device__ __forceinline__ void raise_max(float m_new) {
     if (__ballot(m_new > m) != 0) {
       // a column whose max did not move keeps its scale (also when both are -inf)
       const float alpha = kCols ? (m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f)
@@ -402,6 +454,12 @@ struct HeadState {
       for (int t = 0; t < kE; ++t) acc[t] *= alpha;
       m = m_new;
     }
+  }
+
+  // The block's probabilities against the running max, added to l; returns
+  // them as the bf16 P operand of the P.V MFMAs.
+  template <bool kCols>
+  __device__ __forceinline__ short4_t probs(const float* sv, float vs) {
     // a column that has seen no token yet has m = -inf and all logits -inf
     const float mref = (kCols && m == -INFINITY) ? 0.0f : m;
     float p[4];
@@ -412,14 +470,17 @@ struct HeadState {
     // product (folding it into the bf16 P would put a relative 2^-9 error on
     // every V row); a bf16 cache has no V scale (callers pass vs = 1)
     const uint2 pbits = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    const short4_t pop = __builtin_bit_cast(short4_t, pbits);
     if constexpr (kInt4) {
       // the P.V MFMA sees V + 136: keep V scale * (sum of the bf16 P it used) to take off at the end
       const float ps = (bf16_bits_to_f32(pbits.x & 0xffffu) + bf16_bits_to_f32(pbits.x >> 16)) +
                        (bf16_bits_to_f32(pbits.y & 0xffffu) + bf16_bits_to_f32(pbits.y >> 16));
       vbias = __builtin_fmaf(sum_xor16(sum_xor32(ps)), vs, vbias);
     }
-    // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n)
+    return __builtin_bit_cast(short4_t, pbits);
+  }
+
+  // ---- O^T += V^T . P^T, one MFMA per d tile n (d = kE*r + n)
+  __device__ __forceinline__ void pv(const VOperands<D, kFmt>& vo, short4_t pop, float vs) {
 #pragma unroll
     for (int nn = 0; nn < kE; ++nn) {
       if constexpr (T::kScaled) {
@@ -452,6 +513,38 @@ struct HeadState {
       for (int j = 0; j < 4; ++j) o[kE * j + nn] = kInt4 ? acc[nn][j] - vb : acc[nn][j];
   }
 };
+
+// Fold one block into two tiles of columns (step_cols of each), phase by
+// phase: both tiles' QK products, then both softmax updates, then both P.V
+// products, so that one tile's MFMAs run under the other's vector work.
+// The K operand is converted once for both.
+template <int D, int kFmt>
+__device__ __forceinline__ void step_cols2(HeadState<D, kFmt>& ha, HeadState<D, kFmt>& hb, const BlockRegs<D, kFmt>& br,
+                                           const VOperands<D, kFmt>& vo, int valid, int col_valid_a, int col_valid_b,
+                                           float sc, float vs, int c) {
+  using H = HeadState<D, kFmt>;
+  f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int st = 0; st < Tile<D, kFmt>::kKSteps; ++st) {
+    const bf16x8_t k = H::k_operand(br, st);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, ha.qop[st], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, hb.qop[st], sb, 0, 0, 0);
+  }
+  float xa[4], xb[4];
+  ha.logits(sa, sc, xa);
+  hb.logits(sb, sc, xb);
+  // one wave-uniform test for the context end and both tiles' horizons
+  if (valid < kBlockTokens || __ballot(col_valid_a < kBlockTokens || col_valid_b < kBlockTokens) != 0) {
+    H::hide_tokens(xa, min(valid, col_valid_a), c);
+    H::hide_tokens(xb, min(valid, col_valid_b), c);
+  }
+  const float ma = fmaxf(ha.m, H::block_max(xa)), mb = fmaxf(hb.m, H::block_max(xb));
+  ha.template raise_max<true>(ma);
+  hb.template raise_max<true>(mb);
+  const short4_t pa = ha.template probs<true>(xa, vs), pb = hb.template probs<true>(xb, vs);
+  ha.pv(vo, pa, vs);
+  hb.pv(vo, pb, vs);
+}
 
 // Finished rows leave a wave through LDS, this many rows per pass.
 constexpr int kStageRows = 8;

@@ -139,7 +139,7 @@ struct PlanMergeRow {
 struct PlanWideGroup {
   int32_t item0, nitems, blk_lo, blk_hi;
 };
-constexpr int kWideTiles = 8;
+constexpr int kWideTiles = 4;
 
 struct PlanLayout {
   size_t items_off, cols_off, rows_off, entries_off, wg_off, wide_off, bytes;

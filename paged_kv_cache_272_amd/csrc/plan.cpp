@@ -28,8 +28,9 @@
 //
 // A segment with many tiles (a prefill chunk: hundreds of query columns
 // over the same blocks) would have each block read once per tile.  Its
-// tiles go to wide groups instead: up to 8 tiles, one workgroup per KV
-// head, one wave per tile, each block read once into LDS for the group.
+// tiles go to wide groups instead: up to kWideTiles (4) items of 32
+// columns, one workgroup per KV head, one wave per item, each block read
+// once into LDS for the group.
 #include <algorithm>
 #include <cstring>
 #include <map>

@@ -175,20 +175,20 @@ def test_shared_prefix_plan_executed_on_cpu_matches_oracle_decode():
 
 def test_prefill_chunk_goes_to_wide_groups():
     """4 chunks of 512 new tokens at 4096 context, group 4: 2048 columns = 64
-    tiles per sequence, 8 wide groups of 8 tiles each; 32 groups x 8 KV heads
-    fill the device, so no run is cut: every item writes its output directly
-    and each KV head reads each block once per group."""
+    items of 32 columns per sequence, 16 wide groups of 4 items each; 64
+    groups x 8 KV heads fill the device, so no run is cut: every item writes
+    its output directly and each KV head reads each block once per group."""
     ctxs, q_lens = [4096] * 4, [512] * 4
     bt = _tables(ctxs, np.random.default_rng(11))
     plan, info = pa.pa_plan_attention(np.array(ctxs), 32, 8, 128, q_start=_q_start(q_lens))
-    assert info.num_wide_groups == 32 and info.num_wgs == 0 and info.num_records == 0
+    assert info.num_wide_groups == 64 and info.num_wgs == 0 and info.num_records == 0
     assert info.num_items == 4 * 64 and info.max_item_columns == 32
     check_slices(plan, info)
     check_coverage(plan, info, _q_start(q_lens), ctxs, bt, 4)
-    # a group's run ends at its last tile's horizon: chunk tokens 64g .. 64g+63 see up to 3584 + 64(g+1)
+    # a group's run ends at its last item's horizon: chunk tokens 32g .. 32g+31 see up to 3584 + 32(g+1)
     wide = unpack_plan(plan, info)["wide"]
-    assert sorted(int(h) for h in wide[:8, 3]) == [(3584 + 64 * (k + 1)) // 16 for k in range(8)]
-    assert info.block_reads == 4 * sum(int(h) for h in wide[:8, 3])
+    assert sorted(int(h) for h in wide[:16, 3]) == [(3584 + 32 * (k + 1)) // 16 for k in range(16)]
+    assert info.block_reads == 4 * sum(int(h) for h in wide[:16, 3])
 
 
 def test_short_prefill_wide_groups_are_cut_into_pieces():
