@@ -262,7 +262,9 @@ __device__ __forceinline__ void load_block_with_row(BlockRegs<D, kFmtBf16>& br, 
 }
 
 template <int D, int kFmt>
-__global__ __launch_bounds__(64 * kBalancedMaxWaves) void decode_mfma_balanced_kernel(DecodeArgs a) {
+// (int4: at least three waves per SIMD, see kBalancedMaxWavesInt4)
+__global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) void decode_mfma_balanced_kernel(
+    DecodeArgs a) {
   constexpr int kE = Tile<D, kFmt>::kE;
   extern __shared__ int s_dyn[];                 // start[B + 1], ctx[B], then per wave kStageRows x D floats
   __shared__ int s_wave_tot[kBalancedMaxWaves];

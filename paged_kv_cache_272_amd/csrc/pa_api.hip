@@ -80,13 +80,18 @@ WorkspaceLayout partition_layout(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 // Balanced split: partial rows (workgroup, slot 0/1, query head), plus the
 // per-sequence unit starts.  One wave per KV head, at most 8 waves per
-// workgroup, about kBalancedTargetWaves waves over the device.
-WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+// workgroup (int4: 4), about kBalancedTargetWaves waves over the device
+// (int4: kBalancedTargetWavesInt4).
+WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                pa_dtype cache_dtype) {
   WorkspaceLayout w;
   w.balanced = true;
-  w.waves_per_wg = num_kv_heads < kBalancedMaxWaves ? num_kv_heads : kBalancedMaxWaves;
+  const bool int4 = cache_dtype == PA_DTYPE_INT4;
+  const int32_t max_waves = int4 ? kBalancedMaxWavesInt4 : kBalancedMaxWaves;
+  const int32_t target = int4 ? kBalancedTargetWavesInt4 : kBalancedTargetWaves;
+  w.waves_per_wg = num_kv_heads < max_waves ? num_kv_heads : max_waves;
   w.head_groups = (num_kv_heads + w.waves_per_wg - 1) / w.waves_per_wg;
-  const int32_t wgs = kBalancedTargetWaves / (w.waves_per_wg * w.head_groups);
+  const int32_t wgs = target / (w.waves_per_wg * w.head_groups);
   w.num_wgs = wgs < 1 ? 1 : wgs;
   const size_t rows = (size_t)w.num_wgs * 2 * num_q_heads;
   w.m_off = 0;
@@ -210,8 +215,10 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   // take: report enough for either split
   size_t bytes = partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).bytes;
   if (use_balanced(PA_DTYPE_BF16, num_seqs, partition_tokens)) {
-    const size_t b2 = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).bytes;
-    bytes = b2 > bytes ? b2 : bytes;
+    for (pa_dtype cd : {PA_DTYPE_BF16, PA_DTYPE_INT4}) {   // (nor the cache type: the larger of the two shapes)
+      const size_t b2 = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, cd).bytes;
+      bytes = b2 > bytes ? b2 : bytes;
+    }
   }
   return bytes;
 }
@@ -243,7 +250,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   if (scaled_dtype(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_MISALIGNED;
   const WorkspaceLayout w = use_balanced(q_dtype, num_seqs, partition_tokens)
-                                ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim)
+                                ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype)
                                 : partition_layout(num_seqs, num_q_heads, head_dim, max_context_len,
                                                    partition_tokens);
   if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return PA_ERR_WORKSPACE;

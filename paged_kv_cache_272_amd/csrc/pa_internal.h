@@ -100,10 +100,15 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge_balanced(const DecodeArgs& a, hipStream_t stream);
 
 // Balanced split: at most this many sequences (their start units live in LDS),
-// about this many waves in flight over the whole device.
+// about this many waves in flight over the whole device, at most this many
+// waves per workgroup.  bf16 and e4m3 caches run two waves per SIMD (8-wave
+// workgroups, up to 256 VGPRs); an int4 cache, bound by vector work rather
+// than HBM, runs three (4-wave workgroups, three per CU, up to 168 VGPRs).
 constexpr int kBalancedMaxSeqs = 4096;
 constexpr int kBalancedTargetWaves = 2048;
 constexpr int kBalancedMaxWaves = 8;
+constexpr int kBalancedTargetWavesInt4 = 3072;
+constexpr int kBalancedMaxWavesInt4 = 4;
 
 // Largest partition the partition kernels accept.
 constexpr int kMaxPartitionTokens = 512;
