@@ -510,7 +510,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the decode shards by sequence or KV head with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
