@@ -278,7 +278,10 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
 // block i+1 is written to one while block i is folded in from the other.
 // Two workgroups share a CU.
 
-constexpr int kWideBufs = 2;
+// LDS block buffers: two alternating buffers of one block, of a pair of
+// blocks for bf16 (which folds blocks in pairs)
+template <int kFmt>
+constexpr int wide_block_bufs() { return kFmt == kFmtBf16 ? 4 : 2; }
 constexpr int kWideAhead = 4;   // blocks in flight per thread (6 and 8 measured no faster)
 
 template <int D, int kFmt>
@@ -308,7 +311,7 @@ template <int D, int kFmt>
 __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(PlannedArgs a) {   // two workgroups per CU
   constexpr int kTiles = 2;
   using L = WideLayout<D, kFmt>;
-  extern __shared__ __align__(16) uint8_t s_wide[];          // kWideBufs block buffers, then the waves' result stages
+  extern __shared__ __align__(16) uint8_t s_wide[];          // block buffers, then the waves' result stages
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, c = lane >> 4;
   // Workgroup b runs on XCD b mod 8.  Logical workgroup j = (KV head, group)
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
   const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
-  float* stage = reinterpret_cast<float*>(s_wide + kWideBufs * L::kBuf) + wave * kStageRows * D;
+  float* stage = reinterpret_cast<float*>(s_wide + wide_block_bufs<kFmt>() * L::kBuf) + wave * kStageRows * D;
 
   // this wave's columns and query rows
   PlanColumn cols[kTiles];
@@ -387,8 +390,11 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
     src_off[k] = (int64_t)prow * L::kRowBytes + pcol * 16;
     lds_off[k] = half * L::kHalf + prow * L::kStride + pcol * 16;
   }
+  // A block's pieces, with its scales taken while its id is in the window
+  // (the window may move on before the block is folded in).
   struct Pieces {
     uint4 v[kPP];
+    float ks, vs;
   };
   auto load_piece = [&](int i) {
     if (i - idbase >= 64) {
@@ -401,6 +407,11 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
 #pragma unroll
     for (int k = 0; k < kPP; ++k)
       pc.v[k] = *reinterpret_cast<const uint4*>((is_v[k] ? vbase : kbase) + head0 + src_off[k]);
+    pc.ks = pc.vs = 1.0f;
+    if constexpr (kFmt != kFmtBf16) {
+      pc.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i - idbase));
+      pc.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i - idbase));
+    }
     return pc;
   };
   auto store_pieces = [&](uint8_t* buf, const Pieces& pc) {
@@ -413,43 +424,94 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
     __builtin_amdgcn_s_barrier();
   };
 
-  // kAhead blocks in flight per thread (a ring of pieces), two LDS buffers.
-  // Step i folds block i in from LDS, having issued the load of block
-  // i + kAhead, and writes block i + 1 (loaded kAhead - 1 steps ago) to the
-  // other buffer.  Every step issues exactly one load (past the run's end a
-  // copy of its last block) so the waits before the writes leave the later
-  // loads in flight.
-  constexpr int kAhead = kWideAhead;
-  auto buf = [&](int i) { return s_wide + ((i - lo) & 1) * L::kBuf; };
-  if (lo < hi) {
-    Pieces ring[kAhead];
+  if constexpr (kFmt == kFmtBf16) {
+    // bf16: blocks go in pairs (step_pair_cols2), kAheadPairs pairs in
+    // flight per thread, two LDS buffers of a pair each.  Step p folds pair p
+    // in from LDS, having issued the loads of pair p + kAheadPairs, and
+    // writes pair p + 1 (loaded kAheadPairs - 1 steps ago) to the other
+    // buffer.  Past the run's end the loads fetch copies of its last block,
+    // so every step issues the same loads.
+    constexpr int kAheadPairs = 2;
+    auto pbuf = [&](int p) { return s_wide + (p & 1) * 2 * L::kBuf; };
+    const int npairs = (hi - lo + 1) / 2;
+    if (lo < hi) {
+      Pieces ring[kAheadPairs][2];
+      auto load_pair = [&](Pieces* pr, int p) {
+        pr[0] = load_piece(min(lo + 2 * p, hi - 1));
+        pr[1] = load_piece(min(lo + 2 * p + 1, hi - 1));
+      };
+      auto store_pair = [&](int p, const Pieces* pr) {
+        store_pieces(pbuf(p), pr[0]);
+        store_pieces(pbuf(p) + L::kBuf, pr[1]);
+      };
 #pragma unroll
-    for (int k = 0; k < kAhead; ++k) ring[k] = load_piece(min(lo + k, hi - 1));
-    store_pieces(buf(lo), ring[0]);
-    lds_barrier();
-    for (int i0 = lo; i0 < hi; i0 += kAhead) {
+      for (int k = 0; k < kAheadPairs; ++k) load_pair(ring[k], k);
+      store_pair(0, ring[0]);
+      lds_barrier();
+      for (int p0 = 0; p0 < npairs; p0 += kAheadPairs) {
 #pragma unroll
-      for (int k = 0; k < kAhead; ++k) {
-        const int i = i0 + k;
-        ring[k] = load_piece(min(i + kAhead, hi - 1));
-        if (i < hi && has_item && i < it_hi) {
-          BlockRegs<D, kFmt> br;
-          load_block_lds<D, kFmt>(br, buf(i), r, c);
-          float ks = 1.0f, vs = 1.0f;
-          if constexpr (kFmt != kFmtBf16) {
-            ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i - idbase));
-            vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i - idbase));
+        for (int k = 0; k < kAheadPairs; ++k) {
+          const int p = p0 + k, i = lo + 2 * p;
+          load_pair(ring[k], p + kAheadPairs);
+          if (p < npairs && has_item && i < it_hi) {
+            const int t0 = i * kBlockTokens;
+            const bool two = i + 1 < it_hi;           // (it_hi <= hi)
+            BlockRegs<D, kFmt> b0, b1;
+            load_block_lds<D, kFmt>(b0, pbuf(p), r, c);
+            load_block_lds<D, kFmt>(b1, pbuf(p) + L::kBuf, r, c);
+            const int valid0 = min(kBlockTokens, it.kv_len - t0);
+            const int valid1 = two ? min(kBlockTokens, it.kv_len - t0 - kBlockTokens) : 0;
+            const VOperands<D, kFmt> v0 = make_voperands<D, kFmt>(b0, valid0, c);
+            const VOperands<D, kFmt> v1 = make_voperands<D, kFmt>(b1, valid1, c);
+            if (second) {
+              step_pair_cols2(hs[0], hs[1], b0, b1, v0, v1, valid0, valid1, horizon[0] - t0,
+                              horizon[0] - t0 - kBlockTokens, horizon[1] - t0, horizon[1] - t0 - kBlockTokens,
+                              a.scale_log2, c);
+            } else {
+              hs[0].step_cols(b0, v0, valid0, horizon[0] - t0, a.scale_log2, 1.0f, c);
+              if (two) hs[0].step_cols(b1, v1, valid1, horizon[0] - t0 - kBlockTokens, a.scale_log2, 1.0f, c);
+            }
           }
-          const int t0 = i * kBlockTokens;
-          const int valid = min(kBlockTokens, it.kv_len - t0);
-          const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(br, valid, c);
-          if (second)
-            step_cols2(hs[0], hs[1], br, vo, valid, horizon[0] - t0, horizon[1] - t0, a.scale_log2 * ks, vs, c);
-          else
-            hs[0].step_cols(br, vo, valid, horizon[0] - t0, a.scale_log2 * ks, vs, c);
+          if (p + 1 < npairs) store_pair(p + 1, ring[(k + 1) % kAheadPairs]);
+          lds_barrier();
         }
-        if (i + 1 < hi) store_pieces(buf(i + 1), ring[(k + 1) % kAhead]);
-        lds_barrier();
+      }
+    }
+  } else {
+    // kAhead blocks in flight per thread (a ring of pieces), two LDS buffers.
+    // Step i folds block i in from LDS, having issued the load of block
+    // i + kAhead, and writes block i + 1 (loaded kAhead - 1 steps ago) to the
+    // other buffer.  Every step issues exactly one load (past the run's end a
+    // copy of its last block) so the waits before the writes leave the later
+    // loads in flight.
+    constexpr int kAhead = kWideAhead;
+    auto buf = [&](int i) { return s_wide + ((i - lo) & 1) * L::kBuf; };
+    if (lo < hi) {
+      Pieces ring[kAhead];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) ring[k] = load_piece(min(lo + k, hi - 1));
+      store_pieces(buf(lo), ring[0]);
+      lds_barrier();
+      for (int i0 = lo; i0 < hi; i0 += kAhead) {
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) {
+          const int i = i0 + k;
+          const float ks = ring[k].ks, vs = ring[k].vs;   // block i's, before the slot is reloaded
+          ring[k] = load_piece(min(i + kAhead, hi - 1));
+          if (i < hi && has_item && i < it_hi) {
+            BlockRegs<D, kFmt> br;
+            load_block_lds<D, kFmt>(br, buf(i), r, c);
+            const int t0 = i * kBlockTokens;
+            const int valid = min(kBlockTokens, it.kv_len - t0);
+            const VOperands<D, kFmt> vo = make_voperands<D, kFmt>(br, valid, c);
+            if (second)
+              step_cols2(hs[0], hs[1], br, vo, valid, horizon[0] - t0, horizon[1] - t0, a.scale_log2 * ks, vs, c);
+            else
+              hs[0].step_cols(br, vo, valid, horizon[0] - t0, a.scale_log2 * ks, vs, c);
+          }
+          if (i + 1 < hi) store_pieces(buf(i + 1), ring[(k + 1) % kAhead]);
+          lds_barrier();
+        }
       }
     }
   }
@@ -537,7 +599,8 @@ hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
 // LDS of a wide workgroup: two block buffers, then a result stage per wave.
 template <int D, int kFmt>
 size_t wide_lds_bytes() {
-  return kWideBufs * (size_t)WideLayout<D, kFmt>::kBuf + (size_t)kWideTiles * kStageRows * D * sizeof(float);
+  return wide_block_bufs<kFmt>() * (size_t)WideLayout<D, kFmt>::kBuf +
+         (size_t)kWideTiles * kStageRows * D * sizeof(float);
 }
 
 hipError_t launch_attend_wide(const PlannedArgs& a, hipStream_t stream) {

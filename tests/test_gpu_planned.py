@@ -103,6 +103,31 @@ def test_prefill_chunk_bench_shape():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
+def test_wide_groups_past_64_blocks(kv):
+    """Wide groups whose block runs cross the kernel's 64-block windows of
+    block ids and scales (runs of 98 to 129 blocks, odd and even counts: the
+    bf16 path folds blocks in pairs); 4 x 512 new tokens at 2055 context
+    fill the device, so no run is cut.  One sequence checked in full."""
+    wl = W.make_multi_query_workload(name="wide64", seed=205, context_lens=[2055] * 4, q_lens=[512] * 4,
+                                     num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype=kv, fp8_mode="values")
+    quantize_fp8_values(wl)
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    k_ref, v_ref = oracle_after_write(wl)
+    seqs = [1]
+    want = oracle.multi_query_ref(wl.q, wl.q_start, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale,
+                                  "bf16", kv, wl.k_scale, wl.v_scale, seqs=seqs)
+    out, info = _run(dw, wl)
+    assert info.num_wide_groups == 64 and info.num_wgs == 0
+    rows = np.arange(wl.q_start[1], wl.q_start[2])
+    got = out_to_f64(out)[rows]
+    err = float(np.abs(got - want[rows]).max())
+    log(f"wide past 64 blocks kv={kv}: max abs error {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL[kv], err
+
+
 def test_decode_through_a_plan_matches_oracle():
     wl = W.make_workload(name="plan-decode", seed=204, context_lens=[1, 17, 600, 1500, 33], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
