@@ -405,7 +405,7 @@ def run_serve(args, pa, torch, np, oracle):
     vn = torch.randn(slots, hkv, d, device="cuda").to(torch.bfloat16)
     out = torch.empty_like(q)
     state = {"next": 0, "waiting": [], "running": [], "left": {}, "ctx": {}, "admitted": 0, "finished": 0,
-             "preempted": 0, "host_s": 0.0, "tokens": 0, "kv_bytes": 0, "util": [], "naive": []}
+             "preempted": 0, "host_s": 0.0, "tokens": 0, "kv_bytes": 0, "util": [], "naive": [], "iters": 0}
 
     def new_request():
         n = int(rng.integers(128, 4097))
@@ -452,10 +452,12 @@ def run_serve(args, pa, torch, np, oracle):
                 state["running"].remove(s)
                 drv.finish(s)
                 state["finished"] += 1
-        st = drv.bm.stats()
-        used = (st["num_blocks"] - st["free_blocks"]) * 16
-        state["util"].append(st["stored_tokens"] / max(used, 1))
-        state["naive"].append(st["logical_tokens"] / max(len(state["running"]) * max_len, 1))
+        state["iters"] += 1
+        if state["iters"] % 8 == 1:           # memory use sampled every 8th iteration
+            st = drv.bm.stats()
+            used = (st["num_blocks"] - st["free_blocks"]) * 16
+            state["util"].append(st["stored_tokens"] / max(used, 1))
+            state["naive"].append(st["logical_tokens"] / max(len(state["running"]) * max_len, 1))
 
     for _ in range(args.warmup):
         iteration()

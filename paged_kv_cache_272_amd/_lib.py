@@ -522,6 +522,11 @@ def prepare_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, 
                                                    context_lens, k_scale, v_scale, workspace))
 
 
+def check_status(status: int, where: str) -> None:
+    """Raise PaError for a non-zero status of an entry point called through raw_call."""
+    _check(status, where)
+
+
 def raw_call(name: str, *args):
     """Call an exported entry point with raw ctypes arguments (for ABI tests)."""
     return getattr(_lib, name)(*args)

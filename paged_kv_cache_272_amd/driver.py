@@ -28,6 +28,8 @@ from ._lib import BLOCK_SIZE, HostBlockManager
 
 
 class DecodeDriver:
+    kHostSets = 8
+    kEventEvery = 4
     def __init__(self, num_blocks: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  max_blocks_per_seq: int, max_batch: int, scale: Optional[float] = None,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", free_order=None):
@@ -40,29 +42,45 @@ class DecodeDriver:
         self.v_cache = torch.empty_like(self.k_cache)
         # The per-iteration arrays share one buffer, [lens | pairs | tables],
         # each section starting on 16 bytes, so that one pa_upload moves the
-        # used prefix to the device copy of the same layout.  Two pinned host
-        # buffers are used in turn; a buffer is refilled only after the
-        # upload that read it has finished.
+        # used prefix to the device copy of the same layout.  kHostSets pinned
+        # host buffers are used in turn; a buffer is refilled only after the
+        # upload that read it has finished.  That is known from an event
+        # recorded after every kEventEvery-th upload (an event between two
+        # kernels costs the stream a few microseconds, so not every step
+        # records one): the one recorded at or after the buffer's last use.
         r16 = lambda n: (n + 3) // 4 * 4  # int32 elements to a multiple of 16 bytes
         self._off_pr = r16(max_batch)
         self._off_bt = self._off_pr + r16(2 * max_batch)
         self._words = self._off_bt + r16(max_batch * max_blocks_per_seq)
         self._host = []
-        for _ in range(2):
+        for _ in range(self.kHostSets):
             buf = torch.zeros(self._words, dtype=torch.int32).pin_memory()
             self._host.append({
                 "buf": buf,
                 "views": self._views(buf),
                 "sl": torch.zeros(max_batch, dtype=torch.int64).pin_memory(),
-                "done": None,
             })
-        self._turn = 0
+        # slot mappings of admitted prompts: two pinned staging buffers in turn
+        # (each reused once the upload that read it has finished), one device copy
+        max_tokens = max_blocks_per_seq * BLOCK_SIZE
+        self._slot_stage = [torch.zeros(max_tokens + 1, dtype=torch.int64).pin_memory() for _ in range(2)]
+        self._slot_event = [torch.cuda.Event() for _ in range(2)]
+        self._slot_used = [False, False]
+        self._slot_turn = 0
+        self._slots_dev = torch.zeros(max_tokens + 1, dtype=torch.int64, device=self.device)
+        self._pos = np.arange(max_tokens, dtype=np.int64)
+        self._events = [torch.cuda.Event() for _ in range(3)]
+        self._event_step = [-1] * 3      # the step whose upload each event follows
+        self._step_no = 0
         self._dev = torch.zeros(self._words, dtype=torch.int32, device=self.device)
         self.cl, self.pr, self.bt = self._views(self._dev)
         ws = _lib.pa_decode_workspace_size(max_batch, num_q_heads, num_kv_heads, head_dim,
                                            max_blocks_per_seq * BLOCK_SIZE, 0)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
         self.last_pairs = 0
+        # marshalled pa_decode_append arguments per (batch, caller tensors, stream):
+        # validated on first use; only max_context_len changes between steps
+        self._calls = {}
 
     def _views(self, buf: torch.Tensor):
         """(lens [max_batch], pairs [max_batch, 2], tables [max_batch, mb]) over a packed buffer."""
@@ -79,10 +97,21 @@ class DecodeDriver:
         self.bm.add(seq, n)
         if n == 0:
             return
+        if n > self._pos.size:
+            raise ValueError("prompt longer than max_blocks_per_seq * 16 tokens")
         table, _ = self.bm.table(seq)
-        pos = np.arange(n, dtype=np.int64)
-        slots = torch.from_numpy(table[pos // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + pos % BLOCK_SIZE)
-        _lib.pa_cache_write(k, v, self.k_cache, self.v_cache, slots.to(self.device, non_blocking=True))
+        turn = self._slot_turn
+        self._slot_turn ^= 1
+        if self._slot_used[turn]:
+            self._slot_event[turn].synchronize()
+        pos = self._pos[:n]
+        stage = self._slot_stage[turn].numpy()
+        np.add(table[pos // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE, pos % BLOCK_SIZE, out=stage[:n])
+        stream = torch.cuda.current_stream(self.device)
+        _lib.pa_upload(self._slots_dev, self._slot_stage[turn], (n * 8 + 15) // 16 * 16, stream=stream.cuda_stream)
+        self._slot_event[turn].record(stream)
+        self._slot_used[turn] = True
+        _lib.pa_cache_write(k, v, self.k_cache, self.v_cache, self._slots_dev[:n], stream=stream.cuda_stream)
 
     def fork(self, parent: int, child: int) -> None:
         self.bm.fork(parent, child)
@@ -101,19 +130,36 @@ class DecodeDriver:
             return
         if b > self.max_batch:
             raise ValueError("batch larger than max_batch")
-        h = self._host[self._turn]
-        self._turn ^= 1
-        if h["done"] is not None:
-            h["done"].synchronize()
+        t = self._step_no
+        h = self._host[t % self.kHostSets]
+        if t >= self.kHostSets:
+            # the upload of step t - kHostSets read this buffer: wait for the
+            # first event recorded after it (one of the last three)
+            need = t - self.kHostSets
+            k = min((k for k in range(3) if self._event_step[k] >= need), key=lambda k: self._event_step[k])
+            self._events[k].synchronize()
         hcl, hpr, hbt = h["views"]
         bt, cl, _, pr = self.bm.step(seqs, self.mb, out=(hbt.numpy(), hcl.numpy(), h["sl"].numpy(), hpr.numpy()))
         npairs = len(pr)
-        _lib.pa_upload(self._dev, h["buf"], (self._off_bt + (b * self.mb + 3) // 4 * 4) * 4)
-        ev = torch.cuda.Event()
-        ev.record()
-        h["done"] = ev
+        stream = torch.cuda.current_stream(self.device)
+        sh = stream.cuda_stream
+        _lib.pa_upload(self._dev, h["buf"], (self._off_bt + (b * self.mb + 3) // 4 * 4) * 4, stream=sh)
+        if t % self.kEventEvery == self.kEventEvery - 1:
+            k = (t // self.kEventEvery) % 3
+            self._events[k].record(stream)
+            self._event_step[k] = t
+        self._step_no = t + 1
         if npairs:
-            _lib.pa_copy_blocks(self.k_cache, self.v_cache, self.pr[:npairs])
+            _lib.pa_copy_blocks(self.k_cache, self.v_cache, self.pr[:npairs], stream=sh)
         self.last_pairs = npairs
-        _lib.pa_decode_append(out, q, k_new, v_new, self.k_cache, self.v_cache, self.bt[:b], self.cl[:b],
-                              int(cl.max()), self.scale, workspace=self.workspace)
+        key = (b, sh, q.dtype, tuple(q.shape), tuple(k_new.shape), tuple(out.shape), q.data_ptr(), k_new.data_ptr(),
+               v_new.data_ptr(), out.data_ptr())
+        args = self._calls.get(key)
+        if args is None:
+            args, _ = _lib._decode_append_args(out, q, k_new, v_new, self.k_cache, self.v_cache, self.bt[:b],
+                                               self.cl[:b], self.mb * BLOCK_SIZE, self.scale, None, None, 0,
+                                               self.workspace, sh)
+            args = list(args)
+            self._calls[key] = args
+        args[13] = int(cl.max())          # max_context_len
+        _lib.check_status(_lib.raw_call("pa_decode_append", *args), "pa_decode_append")
