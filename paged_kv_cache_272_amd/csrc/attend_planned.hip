@@ -535,30 +535,38 @@ __global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(Pla
   const int e0 = clampi(mr.e0, 0, a.num_merge_entries), e1 = clampi(mr.e0 + mr.n, e0, a.num_merge_entries);
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int e = e0; e < e1; e += 4) {
-    float mv[4], lv[4];
-    float4 av[4];
+  constexpr int kBatch = 8;                                     // records whose loads are in flight together
+  for (int e = e0; e < e1; e += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    float4 av[kBatch];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       mv[k] = -INFINITY;
       lv[k] = 0.0f;
       av[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if (e + k < e1) {
+        // the three loads go out together; an empty record's l and acc are
+        // dropped by selection afterwards rather than by a branch on m that
+        // would wait for m before issuing them
         const int64_t wr = (int64_t)g * a.num_records + clampi(a.entries[e + k], 0, a.num_records - 1);
-        mv[k] = a.ws_m[wr];
-        if (mv[k] != -INFINITY) {
-          lv[k] = a.ws_l[wr];
-          av[k] = reinterpret_cast<const float4*>(a.ws_acc + wr * D)[ch];
-        }
+        const float m = a.ws_m[wr];
+        const float l = a.ws_l[wr];
+        const float4 acc = reinterpret_cast<const float4*>(a.ws_acc + wr * D)[ch];
+        const bool seen = m != -INFINITY;
+        mv[k] = m;
+        lv[k] = seen ? l : 0.0f;
+        av[k] = seen ? acc : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
-    const float Mn = fmaxf(M, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) Mn = fmaxf(Mn, mv[k]);
     if (Mn == -INFINITY) continue;                              // nothing seen yet
     const float sc = __builtin_amdgcn_exp2f(M - Mn);            // 0 while M is -inf
     den *= sc;
     num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const float wt = __builtin_amdgcn_exp2f(mv[k] - Mn);      // 0 for empty records
       den += wt * lv[k];
       num.x += wt * av[k].x; num.y += wt * av[k].y; num.z += wt * av[k].z; num.w += wt * av[k].w;

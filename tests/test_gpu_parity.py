@@ -233,8 +233,8 @@ def test_zero_length_sequence_gives_zeros():
 
 
 def test_workspace_reused_across_calls():
-    """The in-kernel merge counters return to zero: one workspace serves many calls
-    and batches of different shapes."""
+    """One workspace serves many calls and batches of different shapes: nothing a
+    call reads from it is left over from an earlier call."""
     wl = W.make_workload(name="reuse", seed=108, context_lens=[3000, 100, 2048, 900, 17], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
     dw = DeviceWorkload(wl)
