@@ -317,11 +317,17 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
   const int g = y * W + wave;
   if (g >= a.num_kv_heads) return;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  // empty sequences own no unit: workgroup 0 writes their zero rows
+  // empty sequences own no unit: workgroup 0 writes their zero rows (64
+  // lengths per look, then the wave writes the rows of each empty one)
   if (x == 0) {
-    for (int b = 0; b < B; ++b)
-      if (s_ctx[b] == 0)
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      unsigned long long empty = __ballot(b0 + lane < B && s_ctx[b0 + lane] == 0);
+      while (empty) {
+        const int b = b0 + __builtin_ctzll(empty);
+        empty &= empty - 1;
         for (int i = lane; i < G * D; i += 64) out[((int64_t)b * a.num_q_heads + (int64_t)g * G) * D + i] = 0;
+      }
+    }
   }
   if (u0 >= u1) return;
 
