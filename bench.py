@@ -26,7 +26,9 @@ fraction of the 8 TB/s HBM spec and of a measured stream-read ceiling, the
 dominant kernel's roofline entry (its algorithmic bytes, or flops for the
 prefill chunk, over its average duration from HIP events recorded on its
 own stream during the timed steps), and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload.  After the timed region it also times steps
+one by one (median and p90) and reports a 'hot' figure with one pool
+reused every step, labelled as such.
 """
 from __future__ import annotations
 
@@ -82,6 +84,9 @@ def parse_args():
     ap.add_argument("--pools", type=int, default=3, help="K/V pool copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dist-steps", type=int, default=100,
+                    help="steps timed one by one after the timed region (median, p90), and steps of the 'hot' "
+                         "figure (one pool reused); 0 skips both")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--timing-every", type=int, default=8,
                     help="record HIP events around the decode kernels of one step in this many")
@@ -501,6 +506,38 @@ def run_serve(args, pa, torch, np, oracle):
     print(json.dumps(result), flush=True)
 
 
+def step_distribution(torch, steps, n):
+    """Median and p90 (us) of n steps, each between two HIP events on the
+    launch stream, rotating the pools as the timed region does."""
+    if n <= 0:
+        return None, None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        for call in steps[i % len(steps)]:
+            call()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return round(us[len(us) // 2], 2), round(us[min(len(us) - 1, (9 * len(us)) // 10)], 2)
+
+
+def hot_step(torch, steps, n):
+    """Mean step time (ms) with the first pool every step: the 'hot' figure."""
+    if n <= 0:
+        return None
+    for _ in range(5):
+        for call in steps[0]:
+            call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        for call in steps[0]:
+            call()
+    torch.cuda.synchronize()
+    return round((time.perf_counter() - t0) / n * 1e3, 5)
+
+
 def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
@@ -556,6 +593,8 @@ def main():
 
     step_s = (t1 - t0) / args.steps
     value = bench.step_bytes / step_s / 1e9
+    dist = step_distribution(torch, steps, args.dist_steps)
+    hot = hot_step(torch, steps, args.dist_steps)
     part_avg_ms = part_ms / max(calls, 1)
     merge_avg_ms = merge_ms / max(calls, 1)
     achieved = bench.kernel_bytes / (part_avg_ms * 1e-3) / 1e9
@@ -597,6 +636,14 @@ def main():
         "measured_stream_read_GBps": round(peak_meas, 1),
         "pct_of_measured_stream_read": round(100 * value / peak_meas, 2),
         "step_algorithmic_bytes": int(bench.step_bytes),
+        "step_us_median": dist[0],
+        "step_us_p90": dist[1],
+        "step_timing": (f"HIP events around each of {args.dist_steps} further steps (after the timed region; "
+                        "the events' own cost is included)"),
+        "hot_ms_per_step": hot,
+        "hot_value": round(bench.step_bytes / (hot * 1e-3) / 1e9, 2) if hot else None,
+        "hot": ("the same K/V pool every step (no rotation): part of it can stay in the 256 MB Infinity "
+                "Cache between steps; reported beside value, never as value"),
         "decode_partition_kernel_ms": round(part_avg_ms, 5),
         "decode_merge_kernel_ms": round(merge_avg_ms, 5),
         "kernel_timing": f"HIP events on the compute stream around {calls} of the {args.steps} timed steps",
