@@ -315,9 +315,26 @@ def build_planned(args, pa, torch, np, W, oracle, name):
     new_k, new_v = _dev(torch, np, wl.new_k, "bf16"), _dev(torch, np, wl.new_v, "bf16")
     bt, slots = _dev(torch, np, wl.block_tables), _dev(torch, np, wl.slot_mapping)
     k0, v0 = _dev(torch, np, wl.k_cache, "bf16"), _dev(torch, np, wl.v_cache, "bf16")
+    copy_rate = None
     if share:
         pairs = _dev(torch, np, wl.copy_pairs.astype(np.int32))
         pa.pa_copy_blocks(k0, v0, pairs)
+        # the copy-on-write call on its own: every pair's K and V block read and
+        # written (repeating it rewrites the same bytes)
+        copy_bytes = 2 * 2 * len(wl.copy_pairs) * wl.num_kv_heads * 16 * wl.head_dim * 2
+        for _ in range(5):
+            pa.pa_copy_blocks(k0, v0, pairs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            pa.pa_copy_blocks(k0, v0, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_us = e0.elapsed_time(e1) / 50 * 1e3
+        copy_rate = {"pairs": int(len(wl.copy_pairs)), "bytes_read_and_written": int(copy_bytes),
+                     "us_per_call": round(copy_us, 2), "GBps": round(copy_bytes / (copy_us * 1e-6) / 1e9, 1),
+                     "timing": "HIP events around 50 back-to-back calls"}
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
     t_plan = time.perf_counter()
     for _ in range(5):
@@ -377,7 +394,7 @@ def build_planned(args, pa, torch, np, W, oracle, name):
         kernel_label=("planned attention kernels (wide groups %d, sliced workgroups %d)"
                       % (info.num_wide_groups, info.num_wgs)),
         data="synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)", config=config,
-        logical_bytes=logical_bytes, cpu_prepare=cpu_prepare, cpu_one=cpu_one,
+        logical_bytes=logical_bytes, copy_blocks=copy_rate, cpu_prepare=cpu_prepare, cpu_one=cpu_one,
         cpu_kind="decode_ref" if share else "multi_query_ref", mfma_bound=name == "chunked_prefill")
 
 
@@ -652,6 +669,8 @@ def main():
     }
     if getattr(bench, "logical_bytes", None):
         result["logical_GBps"] = round(bench.logical_bytes / step_s / 1e9, 1)
+    if getattr(bench, "copy_blocks", None):
+        result["copy_blocks"] = bench.copy_blocks
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
     else:
