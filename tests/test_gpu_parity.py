@@ -197,6 +197,25 @@ def test_many_short_sequences(hq, hkv, d, kv):
     _full_parity(wl, 40, False)
 
 
+@pytest.mark.parametrize("batch", [4096, 4097])
+def test_largest_balanced_batch_and_one_past_it(batch):
+    """4096 sequences is the most the balanced split takes (their unit starts
+    and lengths live in LDS); one more goes through the partition grid.  Both
+    sides of that edge, with the new tokens appended in the same call."""
+    rng = np.random.default_rng(109)
+    lens = rng.integers(1, 48, size=batch)
+    wl = W.make_workload(name=f"batch{batch}", seed=110, context_lens=lens, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    k_ref, v_ref = oracle_after_write(wl)
+    dw.decode_append(pa)
+    torch.cuda.synchronize()
+    seqs = sample_seqs(wl, 64) + [batch - 1]
+    err = decode_error(wl, dw.out, k_ref, v_ref, sorted(set(seqs)))
+    log(f"batch {batch}: decode max abs error {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_empty_sequences_between_live_ones():
     wl = W.make_workload(name="gaps", seed=107, context_lens=[300, 5, 700, 64, 1, 2000, 33, 16], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
