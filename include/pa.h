@@ -443,7 +443,10 @@ const char* pa_status_string(int status);
  * off; sampling keeps the events' own cost out of most calls).
  * pa_timing_read() waits for the recorded events, returns the summed kernel
  * times in milliseconds and the number of calls recorded, and clears the
- * record.  At most 65536 calls are recorded between reads.
+ * record.  At most 65536 calls are recorded between reads.  The events are
+ * timing-only (created without the system-scope fence, so recording them
+ * writes back no caches between the kernels they bracket): they order
+ * nothing and publish no results to the host.
  */
 int pa_timing_enable(int every);
 int pa_timing_read(double* partition_ms, double* merge_ms, int64_t* calls);

@@ -129,8 +129,11 @@ TimingRecord* timing_slot() {
   if (g_timing.seen++ % g_timing.every != 0) return nullptr;
   if (g_timing.used == g_timing.pool.size()) {
     TimingRecord r{};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.mid) != hipSuccess ||
-        hipEventCreate(&r.end) != hipSuccess)
+    // timing-only events: no system-scope fence when they are recorded, so
+    // no cache writeback and invalidation lands between the kernels they time
+    const unsigned f = hipEventDisableSystemFence;
+    if (hipEventCreateWithFlags(&r.start, f) != hipSuccess || hipEventCreateWithFlags(&r.mid, f) != hipSuccess ||
+        hipEventCreateWithFlags(&r.end, f) != hipSuccess)
       return nullptr;
     g_timing.pool.push_back(r);
   }
