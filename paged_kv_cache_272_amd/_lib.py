@@ -149,6 +149,21 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """Scratch that a wrapper allocates for one call.  torch's caching
+    allocator may hand the memory out again once the tensor is released,
+    to work ordered after it on the *current* stream only; when the call
+    runs on another stream, the tensor is marked as used there so that the
+    memory is not reused before that stream's kernels are done with it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+            _stream(stream), device=ws.device)
+        if s.cuda_stream != torch.cuda.current_stream(ws.device).cuda_stream:
+            ws.record_stream(s)
+    return ws
+
+
 def pa_cache_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    slot_mapping: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
                    v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -216,7 +231,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     mb = block_tables.shape[1]
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
                           cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
@@ -236,7 +251,7 @@ def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, co
         raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim] in q's dtype")
     need = pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
             cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
@@ -340,7 +355,7 @@ def pa_attend_planned(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
             or out.shape != q.shape or hkv != info.num_kv_heads or d != info.head_dim:
         raise ValueError("tensor shapes do not match the plan")
     if workspace is None and info.workspace_bytes:
-        workspace = torch.empty(info.workspace_bytes, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(info.workspace_bytes, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pa_attend_planned(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
                                   cache_code(k_cache, info.head_dim), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),

@@ -1,4 +1,5 @@
-// Generic paged decode (VALU): every supported dtype, head_dim and group size.
+// Paged decode on the vector ALUs for an fp32 query and an fp32 cache (the
+// matrix cores take bf16 operands, so this path keeps full fp32 precision).
 //
 // out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b for one query token per
 // sequence ("系统级优化…", section 3.1), where K_b, V_b are gathered page by
@@ -15,6 +16,9 @@
 // Masking: tokens at or past the context length get a score of -inf by
 // selection, and the P.V loop never touches them, so NaN in unused slots
 // cannot reach the output.
+//
+// The merge kernel below also serves the matrix-core partition grid (bf16
+// query), whose partial rows have the same layout.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -24,52 +28,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 16;
 
-enum KvKind { kKvF32 = 0, kKvBf16 = 1, kKvFp8 = 2 };
-
-template <int KV>
-struct KvTraits;
-template <>
-struct KvTraits<kKvF32> { static constexpr int bytes = 4; };
-template <>
-struct KvTraits<kKvBf16> { static constexpr int bytes = 2; };
-template <>
-struct KvTraits<kKvFp8> { static constexpr int bytes = 1; };
-
-// Load N consecutive cache elements (16-byte aligned, N*bytes a multiple of 16) as fp32.
-template <int KV, int N>
-__device__ __forceinline__ void load_elems(const uint8_t* p, float* out) {
-  constexpr int kVec = N * KvTraits<KV>::bytes / 16;
-  const uint4* v = reinterpret_cast<const uint4*>(p);
+// Load N consecutive fp32 cache elements (16-byte aligned, N a multiple of 4).
+template <int N>
+__device__ __forceinline__ void load_elems(const float* p, float* out) {
+  const float4* v = reinterpret_cast<const float4*>(p);
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const uint4 w = v[i];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (KV == kKvF32) {
-        out[i * 4 + j] = __uint_as_float(ws[j]);
-      } else if constexpr (KV == kKvBf16) {
-        out[i * 8 + 2 * j] = bf16_bits_to_f32(ws[j] & 0xffffu);
-        out[i * 8 + 2 * j + 1] = bf16_bits_to_f32(ws[j] >> 16);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) out[i * 16 + 4 * j + k] = e4m3_to_f32((ws[j] >> (8 * k)) & 0xffu);
-      }
-    }
+  for (int i = 0; i < N / 4; ++i) {
+    const float4 w = v[i];
+    out[4 * i] = w.x; out[4 * i + 1] = w.y; out[4 * i + 2] = w.z; out[4 * i + 3] = w.w;
   }
-}
-
-template <int KV>
-__device__ __forceinline__ float load_elem(const uint8_t* base, int64_t idx) {
-  if constexpr (KV == kKvF32) return reinterpret_cast<const float*>(base)[idx];
-  else if constexpr (KV == kKvBf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
-  else return e4m3_to_f32(base[idx]);
-}
-
-template <bool kQBf16>
-__device__ __forceinline__ float load_q(const void* q, int64_t idx) {
-  if constexpr (kQBf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q)[idx]);
-  else return reinterpret_cast<const float*>(q)[idx];
 }
 
 template <bool kQBf16>
@@ -91,10 +58,9 @@ __device__ __forceinline__ int64_t phys_block(const DecodeArgs& a, int b, int lo
   return blk;
 }
 
-template <bool kQBf16, int KV, int D>
+template <int D>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int kDQ = D / 4;            // elements of a K row per lane (4 lanes per token)
-  constexpr int kEb = KvTraits<KV>::bytes;
   __shared__ float q_s[kMaxGroup][D];
   __shared__ float s_s[kMaxGroup][kMaxPartitionTokens];
   __shared__ float m_s[kMaxGroup], l_s[kMaxGroup];
@@ -108,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
   if (ctx == 0) {
     if (part == 0)
-      for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<kQBf16>(a.out, head0 * D + i, 0.0f);
+      for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<false>(a.out, head0 * D + i, 0.0f);
     return;
   }
   const int t0 = part * P;
@@ -116,21 +82,20 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int n = min(P, ctx - t0);
 
   for (int i = threadIdx.x; i < G * D; i += kThreads)
-    q_s[i / D][i % D] = load_q<kQBf16>(a.q, head0 * D + i) * a.scale_log2;
+    q_s[i / D][i % D] = reinterpret_cast<const float*>(a.q)[head0 * D + i] * a.scale_log2;
   __syncthreads();
 
   // Phase 1: scores.  Wave w takes blocks w, w+4, ...; lane -> (token lane/4, quarter lane%4).
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int tok = lane / 4, quarter = lane % 4;
   const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const float* kbase = reinterpret_cast<const float*>(a.k_cache);
   for (int i = wave; i < nblk; i += 4) {
     const int logical = t0 / kBlockTokens + i;
     const int64_t phys = phys_block(a, b, logical);
     const int64_t row = ((phys * a.num_kv_heads + g) * kBlockTokens + tok) * D + quarter * kDQ;
     float kv[kDQ];
-    load_elems<KV, kDQ>(kbase + row * kEb, kv);
-    const float ks = (KV == kKvFp8) ? a.k_scale[phys * a.num_kv_heads + g] : 1.0f;
+    load_elems<kDQ>(kbase + row, kv);
     const int t = i * kBlockTokens + tok;   // token index inside the partition
     for (int h = 0; h < G; ++h) {
       float acc = 0.0f;
@@ -138,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int d = 0; d < kDQ; ++d) acc += q_s[h][quarter * kDQ + d] * kv[d];
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
-      if (quarter == 0) s_s[h][t] = (t < n) ? acc * ks : -INFINITY;
+      if (quarter == 0) s_s[h][t] = (t < n) ? acc : -INFINITY;
     }
   }
   __syncthreads();
@@ -166,14 +131,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   float acc[kMaxPer];
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j) acc[j] = 0.0f;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+  const float* vbase = reinterpret_cast<const float*>(a.v_cache);
   for (int i = 0; i < nblk; ++i) {
     const int64_t phys = phys_block(a, b, t0 / kBlockTokens + i);
-    const float vs = (KV == kKvFp8) ? a.v_scale[phys * a.num_kv_heads + g] : 1.0f;
     const int64_t base = (phys * a.num_kv_heads + g) * kBlockTokens * D + d;
     const int tn = min(kBlockTokens, n - i * kBlockTokens);
     for (int tt = 0; tt < tn; ++tt) {
-      const float v = load_elem<KV>(vbase, base + (int64_t)tt * D) * vs;
+      const float v = vbase[base + (int64_t)tt * D];
       const int t = i * kBlockTokens + tt;
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j) {
@@ -187,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
       const int h = hs + j * kHS;
-      if (h < G) store_out<kQBf16>(a.out, (head0 + h) * D + d, acc[j] / l_s[h]);
+      if (h < G) store_out<false>(a.out, (head0 + h) * D + d, acc[j] / l_s[h]);
     }
   } else {
 #pragma unroll
@@ -281,27 +245,20 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   store_out<kQBf16>(a.out, o + 3, nn.w * inv);
 }
 
-template <bool kQBf16, int KV>
 hipError_t launch_valu(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<kQBf16, KV, 64>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<64>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_valu_kernel<kQBf16, KV, 128>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<128>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
-  if (a.q_dtype == PA_DTYPE_F32) return launch_valu<false, kKvF32>(a, stream);
+  if (a.q_dtype == PA_DTYPE_F32) return launch_valu(a, stream);
   return launch_decode_mfma(a, stream);
-}
-
-hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
-  if (a.q_dtype == PA_DTYPE_F32) return launch_valu<false, kKvF32>(a, stream);
-  if (a.cache_dtype == PA_DTYPE_BF16) return launch_valu<true, kKvBf16>(a, stream);
-  return launch_valu<true, kKvFp8>(a, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
