@@ -545,6 +545,17 @@ def check_int4_encode_bruteforce():
         assert int(c) - 8 == want, (float(x), int(c) - 8, want)
 
 
+def check_int4_nonfinite():
+    """NaN has no int4 code: it is stored as -8, the value the clamp gives it
+    under IEEE-754 maxNum/minNum (which return the operand that is not NaN);
+    infinities saturate.  torch.fmax/fmin implement those two operations."""
+    xs = np.array([np.nan, -np.nan, np.inf, -np.inf, 7.5, 8.5, -8.5, -9.0, 1e30, -1e30], np.float32)
+    t = torch.from_numpy(xs.astype(np.float64))
+    want = (torch.fmin(torch.fmax(torch.round(t), torch.tensor(-8.0)), torch.tensor(7.0)) + 8).to(torch.uint8).numpy()
+    assert np.array_equal(fm.int4_encode(xs), want), (fm.int4_encode(xs), want)
+    assert int(fm.int4_encode(np.array([np.nan], np.float32))[0]) == 0
+
+
 def check_int4_layout():
     """Element 2i is the low nibble of byte i; stored code = value + 8."""
     assert list(fm.int4_to_f64(np.array([0x1F, 0x80], np.uint8))) == [7.0, -7.0, -8.0, 0.0]
@@ -591,6 +602,6 @@ ALL_CHECKS = [
     check_e4m3_encode_vs_torch, check_e4m3_quantize_division, check_bf16_vs_torch,
     check_fp8_scaled_decode, check_cache_write_vs_contiguous_append, check_copy_blocks,
     check_multi_query_full_prefill_vs_sdpa_causal, check_multi_query_vs_python_bruteforce,
-    check_multi_query_chunking_and_decode, check_int4_encode_bruteforce, check_int4_layout,
+    check_multi_query_chunking_and_decode, check_int4_encode_bruteforce, check_int4_nonfinite, check_int4_layout,
     check_int4_decode_vs_sdpa,
 ]

@@ -153,6 +153,15 @@ def _int4_encode_truncating(x):
     return (np.clip(t, -8, 7) + 8).astype(np.uint8)
 
 
+_real_int4_encode = fm.int4_encode
+
+
+def _int4_encode_nan_to_zero(x):
+    x = np.asarray(x, dtype=np.float32)
+    codes = _real_int4_encode(x)
+    return np.where(np.isnan(x), np.uint8(8), codes).astype(np.uint8)
+
+
 MUTANTS = {
     "gqa_modulo_mapping": (pa, "attend", _attend_mutant(gqa="mod")),
     "scale_dropped": (pa, "attend", _attend_mutant(use_scale=False)),
@@ -175,6 +184,7 @@ MUTANTS = {
     "int4_nibble_order": (fm, "int4_unpack", _unpack_high_first),
     "int4_offset_7": (fm, "int4_to_f64", _int4_offset_7),
     "int4_truncating": (fm, "int4_encode", _int4_encode_truncating),
+    "int4_nan_to_zero": (fm, "int4_encode", _int4_encode_nan_to_zero),
 }
 
 
