@@ -10,8 +10,7 @@ import torch
 
 import oracle
 import pa_workloads as W
-
-TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2, "int4": 1e-2}
+from parity import TOL, parity_error
 
 
 def log(msg: str) -> None:
@@ -119,5 +118,4 @@ def decode_error(wl: W.PagedWorkload, out_dev: torch.Tensor, k_host, v_host, seq
     got = out_to_f64(out_dev)[seqs]
     want = oracle.decode_ref(wl.q, k_host, v_host, wl.block_tables, wl.context_lens, wl.scale, wl.q_dtype,
                              wl.kv_dtype, wl.k_scale, wl.v_scale, seqs=seqs)
-    assert np.isfinite(got).all(), "non-finite output"
-    return float(np.abs(got - want).max())
+    return parity_error(got, want)
