@@ -23,7 +23,10 @@
  *   block_pairs     [num_pairs, 2] int32 (src, dst)
  *
  * Ownership: every array argument is device memory owned by the caller.
- * The library allocates no device memory and keeps no per-call state.
+ * The library allocates no device memory at run time and keeps no per-call
+ * state; the only device memory it owns is the static scratch array of
+ * pa_decode_noalloc (one per device, created when the library's code is
+ * loaded onto that device).
  * All calls enqueue work on `stream` (a hipStream_t; NULL = the default
  * stream) and return without synchronising.  The return value reports
  * host-side validation and launch errors only; a fault inside a kernel
@@ -57,6 +60,8 @@ extern "C" {
 #endif
 
 #define PA_BLOCK_SIZE 16
+/* bytes of the static scratch array behind pa_decode_noalloc */
+#define PA_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
 
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
@@ -226,6 +231,33 @@ int pa_decode_append(void* out, const void* q, pa_dtype q_dtype,
                      int32_t head_dim, int32_t num_blocks, float scale,
                      int32_t partition_tokens, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory: code captured into a HIP graph, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * Arguments, results, supported set and errors are those of pa_decode,
+ * without the workspace: the scratch lives in a static device array of
+ * PA_DECODE_NOALLOC_MAX_WORKSPACE bytes (64 MiB) that the library holds on
+ * every device it runs on until the process ends.  Calls whose scratch
+ * (pa_decode_workspace_size) exceeds it return PA_ERR_WORKSPACE before any
+ * launch: every automatic (balanced) split fits; a partition grid fits when
+ * num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes does.
+ * The call allocates nothing and records no timing events.  All calls on
+ * one device share that device's array: calls that may overlap on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller.  The first call on a device looks up that device's copy of the
+ * array (the current device, hipGetDevice).
+ */
+int pa_decode_noalloc(void* out, const void* q, pa_dtype q_dtype,
+                      const void* k_cache, const void* v_cache, pa_dtype cache_dtype,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t num_blocks, float scale,
+                      int32_t partition_tokens, void* stream);
 
 /*
  * pa_copy_blocks — the copy step of copy-on-write.

@@ -70,6 +70,8 @@ _SIGNATURES = {
                                  _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_append": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32,
+                                         _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_upload": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -237,6 +239,28 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                           cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mb,
                           _ptr(context_lens), int(max_context_len), b, hq, hkv, d, num_blocks, float(scale),
                           int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
+
+
+def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      partition_tokens: int = 0, stream=None) -> None:
+    """pa_decode with the library's static scratch (allocates nothing; see include/pa.h)."""
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    b, hq, d = q.shape
+    num_blocks, hkv, bs, _ = k_cache.shape
+    if bs != BLOCK_SIZE or _row(k_cache, d) != d or tuple(out.shape) != (b, hq, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch among q, out and the caches")
+    _check(_lib.pa_decode_noalloc(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache),
+                                  cache_code(k_cache, d), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(context_lens), int(max_context_len), b, hq, hkv, d,
+                                  num_blocks, float(scale), int(partition_tokens), _stream(stream)),
+           "pa_decode_noalloc")
+
+
+# PA_DECODE_NOALLOC_MAX_WORKSPACE (include/pa.h): bytes of pa_decode_noalloc's static scratch
+PA_DECODE_NOALLOC_MAX_WORKSPACE = 64 << 20
 
 
 def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,

@@ -229,12 +229,14 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
 namespace {
 
 // pa_decode and pa_decode_append.  k_new/v_new non-null: appending.
+// need_only non-null: validate every argument except the workspace, store
+// the scratch bytes the call needs there, and launch nothing.
 int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, const void* v_new, const void* k_cache,
                 const void* v_cache, pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool timed = true, size_t* need_only = nullptr) {
   const bool append = k_new != nullptr || v_new != nullptr;
   int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens);
   if (st != PA_OK) return st;
@@ -246,6 +248,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   if (cache_dtype == PA_DTYPE_INT4 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_BAD_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE) return PA_ERR_BAD_SHAPE;
+  if (need_only) *need_only = 0;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
   if (append && (!k_new || !v_new)) return PA_ERR_NULL_POINTER;
@@ -256,6 +259,10 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
                                 ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype)
                                 : partition_layout(num_seqs, num_q_heads, head_dim, max_context_len,
                                                    partition_tokens);
+  if (need_only) {
+    *need_only = w.bytes;
+    return PA_OK;
+  }
   if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return PA_ERR_WORKSPACE;
   if (w.bytes > 0 && !aligned16(workspace)) return PA_ERR_MISALIGNED;
 
@@ -301,7 +308,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
                       max_blocks_per_seq, q_dtype, cache_dtype};
     if (launch_cache_write(cw, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
-  TimingRecord* rec = timing_slot();
+  TimingRecord* rec = timed ? timing_slot() : nullptr;
   if (rec) (void)hipEventRecord(rec->start, s);
   const hipError_t e1 = w.balanced ? launch_decode_mfma_balanced(a, s) : launch_decode_partitions(a, s);
   if (e1 != hipSuccess) return PA_ERR_LAUNCH;
@@ -342,6 +349,76 @@ PA_EXPORT int pa_decode_append(void* out, const void* q, pa_dtype q_dtype, const
   return decode_impl(out, q, q_dtype, k_new, v_new, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, num_blocks, scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+// ---- pa_decode_noalloc: pa_decode with its scratch in a static device array
+//
+// For callers that cannot allocate device memory (work captured into a HIP
+// graph, tight serving loops, harnesses that forbid allocation).  The array
+// below exists once per device the library runs on and lives until the
+// process ends.  In host code its name is only a host-side stand-in: the
+// device address of each device's copy is looked up once with
+// hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.  The decode writes every workspace byte it later reads
+// within the same call, so nothing needs clearing; calls that overlap on one
+// device share the array and therefore race.
+
+namespace pa {
+namespace {
+
+constexpr size_t kStaticScratchBytes = PA_DECODE_NOALLOC_MAX_WORKSPACE;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+} g_scratch;
+
+// The current device's copy of `scratch`, or nullptr (status in *err).
+void* static_scratch(int* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = PA_ERR_LAUNCH;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *err = PA_ERR_LAUNCH;
+      return nullptr;
+    }
+    g_scratch.ptr[dev] = p;
+  }
+  return g_scratch.ptr[dev];
+}
+
+}  // namespace
+}  // namespace pa
+
+PA_EXPORT int pa_decode_noalloc(void* out, const void* q, pa_dtype q_dtype, const void* k_cache, const void* v_cache,
+                                pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t num_blocks, float scale, int32_t partition_tokens,
+                                void* stream) {
+  // every check (the size limit included) before the first HIP call
+  size_t need = 0;
+  const int st = decode_impl(out, q, q_dtype, nullptr, nullptr, k_cache, v_cache, cache_dtype, k_scale, v_scale,
+                             block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                             num_kv_heads, head_dim, num_blocks, scale, partition_tokens, nullptr, 0, stream, false,
+                             &need);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (need > kStaticScratchBytes) return PA_ERR_WORKSPACE;
+  int err = PA_OK;
+  void* ws = static_scratch(&err);
+  if (!ws) return err;
+  return decode_impl(out, q, q_dtype, nullptr, nullptr, k_cache, v_cache, cache_dtype, k_scale, v_scale,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, scale, partition_tokens, ws, kStaticScratchBytes, stream,
+                     false);
 }
 
 PA_EXPORT int pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype cache_dtype, float* k_scale, float* v_scale,

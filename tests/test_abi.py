@@ -90,6 +90,41 @@ def test_decode_validation(kw, status):
     assert decode_call(**kw) == status
 
 
+def noalloc_call(**kw):
+    args = dict(out=FAKE, q=FAKE, q_dtype=BF16, k=FAKE, v=FAKE, cache_dtype=BF16, ks=None, vs=None,
+                bt=FAKE, mb=8192, cl=FAKE, max_ctx=131072, b=8, hq=64, hkv=8, d=128, nb=100000, scale=0.088,
+                part=512)
+    args.update(kw)
+    return lib_mod.raw_call("pa_decode_noalloc", args["out"], args["q"], args["q_dtype"], args["k"], args["v"],
+                            args["cache_dtype"], args["ks"], args["vs"], args["bt"], args["mb"], args["cl"],
+                            args["max_ctx"], args["b"], args["hq"], args["hkv"], args["d"], args["nb"],
+                            args["scale"], args["part"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), WS),                           # 8 x 64 heads x 256 partitions x 130 floats: 68 MB > 64 MiB
+    (dict(d=96), UNSUP),
+    (dict(hq=30), SHAPE),
+    (dict(out=None), NULL),
+    (dict(q=FAKE + 8), ALIGN),
+    (dict(cache_dtype=FP8), NULL),
+    (dict(b=0), OK),
+])
+def test_decode_noalloc_validation(kw, status):
+    """Every rejection happens on the host before any HIP call (no GPU here)."""
+    assert noalloc_call(**kw) == status
+
+
+def test_noalloc_limit_matches_workspace_sizes():
+    """The static scratch holds every balanced split, and the limit sits where the header says."""
+    limit = lib_mod.PA_DECODE_NOALLOC_MAX_WORKSPACE
+    for hq, hkv in ((32, 8), (64, 8), (128, 8), (16, 1), (32, 2), (256, 16)):
+        # (a 512-token bound keeps the partition grid's share of this size query at zero)
+        assert 0 < lib_mod.pa_decode_workspace_size(4096, hq, hkv, 128, 512, 0) <= limit
+    assert lib_mod.pa_decode_workspace_size(8, 64, 8, 128, 131072, 512) > limit
+    assert lib_mod.pa_decode_workspace_size(6, 64, 8, 128, 131072, 512) <= limit
+
+
 def test_workspace_size_and_partition_queries():
     # one partition of 512 tokens holds every sequence: no scratch
     assert lib_mod.pa_decode_workspace_size(64, 32, 8, 128, 512, 512) == 0

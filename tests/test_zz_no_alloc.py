@@ -1,0 +1,68 @@
+"""pa_decode_noalloc (scratch in the library's static device array) against
+pa_decode (caller's workspace), both through the C ABI.
+
+Two calls in a row share the static array, the second with a smaller batch
+(fewer sequences, fewer 16-token units than the split has slices), so a
+second call that read rows left by the first would show.  The outputs must
+equal pa_decode's bit for bit (same kernels, same launch) and the oracle's
+within the decode bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import host_oracle as H
+import pa_workloads as W
+from pa_workloads.configs import config2_lengths
+from gpu_util import DeviceWorkload, log, out_to_f64
+from parity import TOL, parity_error
+
+pytestmark = pytest.mark.gpu
+pa = pytest.importorskip("paged_kv_cache_272_amd")
+
+
+def _pair(wl, partition_tokens):
+    """(pa_decode_noalloc output, pa_decode output) on one device workload."""
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    out_na = torch.full_like(dw.q, float("nan"))
+    log(f"pa_decode_noalloc {wl.name}: B={wl.num_seqs} kv={wl.kv_dtype} partition_tokens={partition_tokens}")
+    pa.pa_decode_noalloc(out_na, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens,
+                         wl.max_context_len, wl.scale, dw.k_scale, dw.v_scale, partition_tokens)
+    torch.cuda.synchronize()
+    out_ws = dw.decode(pa, partition_tokens=partition_tokens, out=torch.full_like(dw.q, float("nan")))
+    torch.cuda.synchronize()
+    return dw, out_na, out_ws
+
+
+def _check(wl, partition_tokens):
+    H.quantize_values(wl)
+    dw, out_na, out_ws = _pair(wl, partition_tokens)
+    assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16)), "differs from pa_decode"
+    k_ref, v_ref = H.after_write(wl)
+    err = parity_error(out_to_f64(out_na), H.decode(wl, k_ref, v_ref))
+    log(f"max abs error against the oracle {err:.3e}")
+    assert err <= TOL[wl.kv_dtype]
+
+
+@pytest.mark.parametrize("kv,part", [("bf16", 0), ("fp8", 0), ("bf16", 256)])
+def test_noalloc_equals_pa_decode_two_calls_second_smaller(kv, part):
+    big = W.make_workload(name="noalloc-big", seed=501, context_lens=config2_lengths(np.random.default_rng(5), 64),
+                          num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv)
+    small = W.make_workload(name="noalloc-small", seed=502, context_lens=[40, 3, 700, 17, 1], num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv)
+    for wl in (big, small):
+        _check(wl, part)
+
+
+def test_noalloc_rejects_scratch_beyond_its_array():
+    """The long-context batch through 512-token partitions needs 68 MB of
+    scratch: rejected before any launch (the balanced split fits)."""
+    q = torch.zeros(8, 64, 128, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(4, 8, 16, 128, dtype=torch.uint8, device="cuda")
+    sc = torch.ones(4, 8, dtype=torch.float32, device="cuda")
+    bt = torch.zeros(8, 8192, dtype=torch.int32, device="cuda")
+    cl = torch.full((8,), 131072, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_noalloc(q, q, kc, kc, bt, cl, 131072, 0.088, sc, sc, 512)
+    assert e.value.status == -5
