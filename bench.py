@@ -225,8 +225,9 @@ def build_decode(args, pa, torch, np, W, oracle, name):
         return W.make_workload(name="llama3_8b_int4", seed=2, context_lens=[int(c) for c in base.context_lens],
                                num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="int4",
                                fp8_mode="codes")
-    wl = {"decode_8b": W.config2, "decode_70b": W.config3, "long_ctx_fp8": W.config5,
-          "decode_8b_int4": int4_8b}[name]()
+    if name == "long_ctx_fp8":
+        return build_long_context(args, pa, torch, np, oracle)
+    wl = {"decode_8b": W.config2, "decode_70b": W.config3, "decode_8b_int4": int4_8b}[name]()
     kv = wl.kv_dtype
     q = _dev(torch, np, wl.q, "bf16")
     new_k, new_v = _dev(torch, np, wl.new_k, "bf16"), _dev(torch, np, wl.new_v, "bf16")
@@ -235,6 +236,12 @@ def build_decode(args, pa, torch, np, W, oracle, name):
                                                                             kv if kv == "bf16" else None)
     ks = None if wl.k_scale is None else _dev(torch, np, wl.k_scale)
     vs = None if wl.v_scale is None else _dev(torch, np, wl.v_scale)
+    return _decode_bench(args, pa, torch, np, oracle, name, wl, q, new_k, new_v, bt, cl, slots, k0, v0, ks, vs)
+
+
+def _decode_bench(args, pa, torch, np, oracle, name, wl, q, new_k, new_v, bt, cl, slots, k0, v0, ks, vs,
+                  data=None, cpu_wl=None):
+    kv = wl.kv_dtype
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.pools - 1)]
     out = torch.empty_like(q)
     ws_bytes = pa.pa_decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
@@ -263,25 +270,33 @@ def build_decode(args, pa, torch, np, W, oracle, name):
               "decode_8b_int4": ("llama3_8b_shape_int4_decode_bs64", "U{128..4096}")}[name]
     k_ref = v_ref = None
 
+    # the CPU oracle's sample: the workload itself, or (long context) a host
+    # copy of some of its sequences (cpu_wl() builds it)
+    host = {}
+
     def cpu_prepare():
-        nonlocal k_ref, v_ref
-        k_ref, v_ref = oracle.cache_write_ref(wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.slot_mapping,
-                                              "bf16", kv, wl.k_scale, wl.v_scale)
+        h = wl if cpu_wl is None else cpu_wl()
+        host["wl"] = h
+        host["ref"] = oracle.cache_write_ref(h.k_cache, h.v_cache, h.new_k, h.new_v, h.slot_mapping, "bf16", kv,
+                                             h.k_scale, h.v_scale)
 
     def cpu_one(b):
-        oracle.decode_ref(wl.q, k_ref, v_ref, wl.block_tables, wl.context_lens, wl.scale, "bf16", kv,
-                          wl.k_scale, wl.v_scale, seqs=[b])
-        return oracle.decode_algorithmic_bytes(wl.context_lens[b:b + 1], wl.num_q_heads, wl.num_kv_heads,
-                                               wl.head_dim, eb, 2, 2, fp8_scales=scaled)
+        h = host["wl"]
+        b = b % h.num_seqs
+        k_ref, v_ref = host["ref"]
+        oracle.decode_ref(h.q, k_ref, v_ref, h.block_tables, h.context_lens, h.scale, "bf16", kv,
+                          h.k_scale, h.v_scale, seqs=[b])
+        return oracle.decode_algorithmic_bytes(h.context_lens[b:b + 1], h.num_q_heads, h.num_kv_heads,
+                                               h.head_dim, eb, 2, 2, fp8_scales=scaled)
 
     return Bench(
         workload=labels[0], steps=steps, pools=len(pools), step_bytes=decode_bytes + write_bytes,
         kernel_bytes=decode_bytes, kernel_flops=None, num_seqs=wl.num_seqs, dtype="bf16" if kv == "bf16" else kv,
         kernel_label="decode partition kernel",
-        data=("synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)" if kv == "bf16" else
-              "synthetic (seeded bf16 q, random finite e4m3 codes with per-(block, head) scales 2^U(-8,-6))"
-              if kv == "fp8" else
-              "synthetic (seeded bf16 q, random int4 codes with per-(block, head) scales 2^U(-4,-2))"),
+        data=data or ("synthetic (seeded N(0,1)*0.5 bf16 q/K/V, shuffled 16-token block pool)" if kv == "bf16" else
+                      "synthetic (seeded bf16 q, random finite e4m3 codes with per-(block, head) scales 2^U(-8,-6))"
+                      if kv == "fp8" else
+                      "synthetic (seeded bf16 q, random int4 codes with per-(block, head) scales 2^U(-4,-2))"),
         config={"workload": labels[0], "batch": wl.num_seqs, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                 "head_dim": wl.head_dim, "block_size": 16, "context_lens": labels[1],
                 "sum_context": int(wl.context_lens.sum()), "kv_dtype": kv, "pool_blocks": wl.num_blocks,
@@ -291,6 +306,52 @@ def build_decode(args, pa, torch, np, W, oracle, name):
                 "step": (f"pa_decode_append: slot write of the {wl.num_seqs} new tokens fused into the decode"
                          if args.step == "append" else f"pa_cache_write({wl.num_seqs} tokens) + pa_decode")},
         cpu_prepare=cpu_prepare, cpu_one=cpu_one, cpu_kind="decode_ref")
+
+
+def build_long_context(args, pa, torch, np, oracle):
+    """Long-context e4m3 decode as stated: 8 x 131072 tokens, K/V N(0,1)*0.5
+    drawn sequence by sequence and quantised to e4m3 on the GPU by the
+    self-scaling scatter (whole blocks: one amax/448 scale per (block, KV
+    head)); the newest token of each sequence is then written by the decode
+    step itself."""
+    from concurrent.futures import ThreadPoolExecutor
+    from pa_workloads import structured as S
+    swl = S.config5_sequence_major("normal")
+    lay = swl.layout
+    nb, hkv, d = swl.num_blocks, swl.num_kv_heads, swl.head_dim
+    k0 = torch.full((nb, hkv, 16, d), 0x7F, dtype=torch.uint8, device="cuda")
+    v0 = torch.full_like(k0, 0x7F)
+    ks = torch.ones(nb, hkv, dtype=torch.float32, device="cuda")
+    vs = torch.ones_like(ks)
+    new_k = np.empty((swl.num_seqs, hkv, d), np.uint16)
+    new_v = np.empty_like(new_k)
+    for b, k, v in swl.iter_values():
+        ctx = int(swl.context_lens[b])
+        pos = np.arange(ctx, dtype=np.int64)
+        slots_b = lay.block_tables[b, pos // 16].astype(np.int64) * 16 + pos % 16
+        pa.pa_cache_write_autoscale(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), k0, v0, ks, vs,
+                                    torch.from_numpy(slots_b).cuda())
+        new_k[b], new_v[b] = S.to_bf16_bits(k[ctx - 1]), S.to_bf16_bits(v[ctx - 1])
+        del k, v
+    torch.cuda.synchronize()
+    lay.q, lay.new_k, lay.new_v, lay.kv_dtype = swl.q, new_k, new_v, "fp8"
+    q = _dev(torch, np, swl.q, "bf16")
+    dnk, dnv = _dev(torch, np, new_k, "bf16"), _dev(torch, np, new_v, "bf16")
+    bt, cl = _dev(torch, np, lay.block_tables), _dev(torch, np, lay.context_lens)
+    slots = _dev(torch, np, lay.slot_mapping)
+
+    def cpu_wl():
+        # two sequences, quantised on the host by the oracle (input preparation, not timed)
+        h = S.materialize(swl, [0, 1], compact=True)
+        with ThreadPoolExecutor(S.default_workers()) as ex:
+            h.k_cache, h.v_cache = ex.map(lambda t: oracle.quantize_pool_ref(*t, "fp8"),
+                                          [(h.k_values, h.k_scale), (h.v_values, h.v_scale)])
+        return h
+
+    data = ("synthetic (seeded: bf16 q N(0,1)*0.5; K/V N(0,1)*0.5 drawn per sequence, quantised to e4m3 on the "
+            "GPU by pa_cache_write_autoscale with one amax/448 scale per (block, KV head))")
+    return _decode_bench(args, pa, torch, np, oracle, "long_ctx_fp8", lay, q, dnk, dnv, bt, cl, slots, k0, v0, ks,
+                         vs, data=data, cpu_wl=cpu_wl)
 
 
 def build_planned(args, pa, torch, np, W, oracle, name):
