@@ -9,9 +9,10 @@
 //        chunk for k-step i and lane group c is (D/32)*c + i, so a lane reads
 //        one contiguous D/4-element run of its token's row.
 //        Result: lane holds s[j] = S^T[token 4c+j][column r], j = 0..3.
-//   softmax: scale, mask by select, block max over the 4 lane groups
-//        (permlane swaps), running max / sum update; the output is rescaled
-//        only when some running max grew.
+//   softmax: logits taken relative to a per-column reference max by one
+//        FMA, mask by select; the reference moves (and the output is
+//        rescaled) only when a logit exceeds it by more than 2^kLazyMax,
+//        which the lane's own maximum shows without any cross-lane step.
 //   PV:  O^T[d][column] += V^T[d][token] . P^T[token][column] with D/16
 //        MFMAs 16x16x16 bf16.  B = P^T: lane holds p[j] for tokens 4c..4c+3
 //        of column r, which is exactly the QK result layout, so P never
@@ -288,6 +289,12 @@ __device__ __forceinline__ VOperands<D, kFmt> make_voperands(const BlockRegs<D, 
   return vo;
 }
 
+// Probabilities are formed against a per-column reference max m (base 2)
+// that moves only when a logit exceeds it by more than this: p = 2^(x - m)
+// may reach 2^kLazyMax, harmless in fp32 and in bf16 (whose exponent range
+// is fp32's), and the final division by l cancels the choice of m exactly.
+constexpr float kLazyMax = 8.0f;
+
 // Running state of one wave: G query heads of one KV head over a run of blocks.
 template <int D, int kFmt>
 struct HeadState {
@@ -296,7 +303,9 @@ struct HeadState {
   static constexpr bool kInt4 = kFmt == kFmtInt4;
   bf16x8_t qop[T::kKSteps];
   f32x4_t acc[kE];
-  float m, l;
+  float m, l;    // reference max (-inf until the column sees a token) and the sum of 2^(x - m)
+  float nm;      // -m, or 0 while m = -inf: the offset of the FMA that forms relative logits
+  float thr;     // a relative logit above this moves the reference: kLazyMax, or -inf while m = -inf
   float qbias;   // int4: 136 * (sum of this lane's query column): removed from every logit
   bool qbias_pending = false;   // int4: qbias still to be taken (begin_row)
   float vbias;   // int4: sum over blocks of V scale * (sum of the block's bf16 P), rescaled like acc
@@ -350,6 +359,8 @@ struct HeadState {
 
   __device__ __forceinline__ void reset() {
     m = -INFINITY;
+    nm = 0.0f;
+    thr = -INFINITY;
     l = 0.0f;
     vbias = 0.0f;
 #pragma unroll
@@ -383,16 +394,16 @@ struct HeadState {
 #pragma unroll
     for (int st = 0; st < T::kKSteps; ++st)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(br, st), qop[st], s, 0, 0, 0);
-    float sv[4];
-    logits(s, sc, sv);
-    if (valid < kBlockTokens) hide_tokens(sv, valid, c);
+    float x[4];
+    rel_logits(s, sc, x);
+    if (valid < kBlockTokens) hide_tokens(x, valid, c);
     if constexpr (kCols) {
       // (a block every column sees in full needs no mask: wave-uniform test)
-      if (__ballot(col_valid < kBlockTokens) != 0) hide_tokens(sv, col_valid, c);
+      if (__ballot(col_valid < kBlockTokens) != 0) hide_tokens(x, col_valid, c);
     }
     // ---- online softmax (base 2)
-    raise_max<kCols>(fmaxf(m, block_max(sv)));
-    const short4_t pop = probs<kCols>(sv, vs);
+    fold<4>(x);
+    const short4_t pop = probs(x, vs);
     pv(vo, pop, vs);
   }
 
@@ -413,58 +424,63 @@ struct HeadState {
     return __builtin_bit_cast(bf16x8_t, kw);
   }
 
-  // Base-2 logits of this lane's 4 scores: times sc (int4: less 136 times
-  // the query sum, the bias the MFMA saw).
-  __device__ __forceinline__ void logits(const f32x4_t& s, float sc, float* sv) {
+  // Base-2 logits of this lane's 4 scores relative to the reference max:
+  // s * sc - m in one FMA (int4: also less 136 times the query sum, the
+  // bias the MFMA saw).
+  __device__ __forceinline__ void rel_logits(const f32x4_t& s, float sc, float* x) {
     if constexpr (kInt4) {
       if (qbias_pending) {
         set_qbias();
         qbias_pending = false;
       }
     }
-    const float sb = -qbias * sc;
+    const float off = kInt4 ? __builtin_fmaf(-qbias, sc, nm) : nm;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sv[j] = kInt4 ? __builtin_fmaf(s[j], sc, sb) : s[j] * sc;
+    for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(s[j], sc, off);
   }
 
   // Remove the block's tokens from `limit` on (this lane's tokens 4c..4c+3).
-  static __device__ __forceinline__ void hide_tokens(float* sv, int limit, int c) {
+  static __device__ __forceinline__ void hide_tokens(float* x, int limit, int c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (4 * c + j >= limit) sv[j] = -INFINITY;
+      if (4 * c + j >= limit) x[j] = -INFINITY;
   }
 
-  // The block's max logit of this lane's column (over the 4 lane groups).
-  static __device__ __forceinline__ float block_max(const float* sv) {
-    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    return max_xor16(max_xor32(mx));
-  }
-
-  // Move the running max to m_new (>= m), rescaling l and acc, if any
-  // column's max grew (wave-uniform test).
-  template <bool kCols>
-  __device__ __forceinline__ void raise_max(float m_new) {
-    if (__ballot(m_new > m) != 0) {
-      // a column whose max did not move keeps its scale (also when both are -inf)
-      const float alpha = kCols ? (m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f)
-                                : __builtin_amdgcn_exp2f(m - m_new);
+  // Take N relative logits of this lane's column into account: if any
+  // exceeds the threshold (wave-uniform test), the columns concerned move
+  // their reference to their maximum over these logits (across the 4 lane
+  // groups), rescale l and the output by 2^(m - m_new), and shift x into
+  // the new frame.  A column that has seen no token keeps m = -inf and
+  // never forms -inf - (-inf).
+  template <int N>
+  __device__ __forceinline__ void fold(float* x) {
+    float lm = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) lm = fmaxf(lm, x[j]);
+    if (__ballot(lm > thr) != 0) {
+      const float bm = max_xor16(max_xor32(lm));          // this column's maximum, relative to m
+      const bool grow = bm > thr;
+      const float m_new = grow ? bm - nm : m;              // (nm = 0 while m = -inf)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
       l *= alpha;
       if constexpr (kInt4) vbias *= alpha;
 #pragma unroll
       for (int t = 0; t < kE; ++t) acc[t] *= alpha;
+      const float shift = grow ? bm : 0.0f;
+#pragma unroll
+      for (int j = 0; j < N; ++j) x[j] -= shift;
       m = m_new;
+      nm = grow ? -m_new : nm;
+      thr = grow ? kLazyMax : thr;
     }
   }
 
-  // The block's probabilities against the running max, added to l; returns
-  // them as the bf16 P operand of the P.V MFMAs.
-  template <bool kCols>
-  __device__ __forceinline__ short4_t probs(const float* sv, float vs) {
-    // a column that has seen no token yet has m = -inf and all logits -inf
-    const float mref = (kCols && m == -INFINITY) ? 0.0f : m;
+  // The block's probabilities 2^x, added to l; returns them as the bf16 P
+  // operand of the P.V MFMAs.
+  __device__ __forceinline__ short4_t probs(const float* x, float vs) {
     float p[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
+    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j]);
     l += (p[0] + p[1]) + (p[2] + p[3]);
     // e4m3/int4: the block's V scale is applied in fp32 to the block's P.V
     // product (folding it into the bf16 P would put a relative 2^-9 error on
@@ -531,17 +547,16 @@ __device__ __forceinline__ void step_cols2(HeadState<D, kFmt>& ha, HeadState<D, 
     sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, hb.qop[st], sb, 0, 0, 0);
   }
   float xa[4], xb[4];
-  ha.logits(sa, sc, xa);
-  hb.logits(sb, sc, xb);
+  ha.rel_logits(sa, sc, xa);
+  hb.rel_logits(sb, sc, xb);
   // one wave-uniform test for the context end and both tiles' horizons
   if (valid < kBlockTokens || __ballot(col_valid_a < kBlockTokens || col_valid_b < kBlockTokens) != 0) {
     H::hide_tokens(xa, min(valid, col_valid_a), c);
     H::hide_tokens(xb, min(valid, col_valid_b), c);
   }
-  const float ma = fmaxf(ha.m, H::block_max(xa)), mb = fmaxf(hb.m, H::block_max(xb));
-  ha.template raise_max<true>(ma);
-  hb.template raise_max<true>(mb);
-  const short4_t pa = ha.template probs<true>(xa, vs), pb = hb.template probs<true>(xb, vs);
+  ha.template fold<4>(xa);
+  hb.template fold<4>(xb);
+  const short4_t pa = ha.probs(xa, vs), pb = hb.probs(xb, vs);
   ha.pv(vo, pa, vs);
   hb.pv(vo, pb, vs);
 }
@@ -570,10 +585,10 @@ __device__ __forceinline__ void step_pair_cols2(HeadState<D, kFmtBf16>& ha, Head
     sb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, hb.qop[st], sb1, 0, 0, 0);
   }
   float xa[8], xb[8];
-  ha.logits(sa0, sc, xa);
-  ha.logits(sa1, sc, xa + 4);
-  hb.logits(sb0, sc, xb);
-  hb.logits(sb1, sc, xb + 4);
+  ha.rel_logits(sa0, sc, xa);
+  ha.rel_logits(sa1, sc, xa + 4);
+  hb.rel_logits(sb0, sc, xb);
+  hb.rel_logits(sb1, sc, xb + 4);
   // one wave-uniform test for the context end and both tiles' horizons in both blocks
   if (valid0 < kBlockTokens || valid1 < kBlockTokens ||
       __ballot(cva0 < kBlockTokens || cva1 < kBlockTokens || cvb0 < kBlockTokens || cvb1 < kBlockTokens) != 0) {
@@ -582,12 +597,10 @@ __device__ __forceinline__ void step_pair_cols2(HeadState<D, kFmtBf16>& ha, Head
     H::hide_tokens(xb, min(valid0, cvb0), c);
     H::hide_tokens(xb + 4, min(valid1, cvb1), c);
   }
-  const float ma = fmaxf(ha.m, fmaxf(H::block_max(xa), H::block_max(xa + 4)));
-  const float mb = fmaxf(hb.m, fmaxf(H::block_max(xb), H::block_max(xb + 4)));
-  ha.template raise_max<true>(ma);
-  hb.template raise_max<true>(mb);
-  const short4_t pa0 = ha.template probs<true>(xa, 1.0f), pa1 = ha.template probs<true>(xa + 4, 1.0f);
-  const short4_t pb0 = hb.template probs<true>(xb, 1.0f), pb1 = hb.template probs<true>(xb + 4, 1.0f);
+  ha.template fold<8>(xa);
+  hb.template fold<8>(xb);
+  const short4_t pa0 = ha.probs(xa, 1.0f), pa1 = ha.probs(xa + 4, 1.0f);
+  const short4_t pb0 = hb.probs(xb, 1.0f), pb1 = hb.probs(xb + 4, 1.0f);
   const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pa0, pa1, 0, 1, 2, 3, 4, 5, 6, 7));
   const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pb0, pb1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
