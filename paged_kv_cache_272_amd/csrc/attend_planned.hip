@@ -81,10 +81,27 @@ __device__ __forceinline__ void load_next(const PlannedArgs& a, const PlanItem& 
 // column).  Records of a KV head are adjacent, so an item's records are
 // consecutive rows; an output row's address comes from the lane that owns
 // its column.
-template <int D, int kFmt, int kTiles>
+// A column's row from tiles in the transposed layout (lane (r, c): dims
+// 16 nn + 4c + i in acc[nn][i]) into a stage row, as bf16 times `inv` or as fp32.
+template <int D>
+__device__ __forceinline__ void stage_tr_bf16(uint16_t* srow, const f32x4_t* acc, int c, float inv) {
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn)
+    *reinterpret_cast<uint2*>(srow + 16 * nn + 4 * c) =
+        make_uint2(pack_bf16x2(acc[nn][0] * inv, acc[nn][1] * inv), pack_bf16x2(acc[nn][2] * inv, acc[nn][3] * inv));
+}
+template <int D>
+__device__ __forceinline__ void stage_tr_f32(float* srow, const f32x4_t* acc, int c) {
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn)
+    *reinterpret_cast<float4*>(srow + 16 * nn + 4 * c) = make_float4(acc[nn][0], acc[nn][1], acc[nn][2], acc[nn][3]);
+}
+
+template <int D, int kFmt, int kTiles, bool kTr = false>
 __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const PlanItem& it,
                                                  const HeadState<D, kFmt> (&hs)[kTiles], const int64_t (&row)[kTiles],
                                                  int ncols, bool second, int g, int lane, float* stage) {
+  static_assert(!kTr || kFmt == kFmtBf16, "transposed tiles carry no int4 bias");
   const int r = lane & 15, c = lane >> 4;
   const int d0 = (D / 4) * c;
 #pragma unroll
@@ -107,7 +124,12 @@ __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const Pla
       const bool mine = r >= rr && r < rr + nr;
       wave_lds_sync();                                      // the previous pass's reads are done
       if (direct) {
-        if (mine) store_bf16_run<D>(reinterpret_cast<uint16_t*>(stage) + (r - rr) * D, d0, o, L > 0.0f ? 1.0f / L : 0.0f);
+        if (mine) {
+          uint16_t* srow = reinterpret_cast<uint16_t*>(stage) + (r - rr) * D;
+          const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+          if constexpr (kTr) stage_tr_bf16<D>(srow, hs[t].acc, c, inv);
+          else store_bf16_run<D>(srow, d0, o, inv);
+        }
         wave_lds_sync();
         for (int pc = lane; pc < nr * D / 8; pc += 64) {
           const int col = rr + pc / (D / 8);
@@ -116,7 +138,10 @@ __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const Pla
               reinterpret_cast<const uint4*>(stage)[pc];
         }
       } else {
-        if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
+        if (mine) {
+          if constexpr (kTr) stage_tr_f32<D>(stage + (r - rr) * D, hs[t].acc, c);
+          else store_f32_run<D>(stage + (r - rr) * D, d0, o);
+        }
         wave_lds_sync();
         float4* dst = reinterpret_cast<float4*>(a.ws_acc + (rec_row0 + rr) * D);
         for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
@@ -284,12 +309,26 @@ template <int kFmt>
 constexpr int wide_block_bufs() { return kFmt == kFmtBf16 ? 4 : 2; }
 constexpr int kWideAhead = 4;   // blocks in flight per thread (6 and 8 measured no faster)
 
+// A bf16 block's P.V operands are read from LDS with transpose reads
+// (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4a + b receives
+// element b of the 8-byte runs addressed by lanes a, a + 4, a + 8, a + 12.
+// Lane (r', c) addressing token 4c + r'/4 at dims 16 nn + 4 (r' % 4) .. + 3
+// thus hands lane (r, c) V[4c .. 4c+3][16 nn + r]: the A operand (V^T) of
+// the P.V MFMA for a tile covering dims 16 nn .. 16 nn + 15, with no
+// register permutes.  The output of such tiles lies transposed: lane (r, c)
+// holds dims 16 nn + 4c + i of column r in acc[nn][i].
+template <int kFmt>
+constexpr bool wide_transposed() { return kFmt == kFmtBf16; }
+
 template <int D, int kFmt>
 struct WideLayout {
   static constexpr int kRowBytes = D * Tile<D, kFmt>::kBits / 8;       // one token row of one head
-  static constexpr int kStride = kRowBytes + 16;                       // padded: rows on different banks
-  static constexpr int kHalf = kBlockTokens * kStride;                 // K (or V) of one block
-  static constexpr int kBuf = 2 * kHalf;                               // K then V
+  // padded rows: K rows (read 16 bytes a lane, a row per lane) 4 banks apart; V
+  // rows for transpose reads (16 lanes read 4 rows x 32 bytes) 8 banks apart
+  static constexpr int kStrideK = kRowBytes + 16;
+  static constexpr int kStrideV = kRowBytes + (wide_transposed<kFmt>() ? 32 : 16);
+  static constexpr int kVOff = kBlockTokens * kStrideK;                // V rows follow the K rows
+  static constexpr int kBuf = kVOff + kBlockTokens * kStrideV;         // K then V of one block
   static constexpr int kPiecesPerRow = kRowBytes / 16;
   static constexpr int kPieces = 2 * kBlockTokens * kPiecesPerRow;     // 16-byte pieces per block, K and V
   static constexpr int kThreads = 64 * kWideTiles;
@@ -301,10 +340,37 @@ template <int D, int kFmt>
 __device__ __forceinline__ void load_block_lds(BlockRegs<D, kFmt>& br, const uint8_t* buf, int r, int c) {
   using T = Tile<D, kFmt>;
   using L = WideLayout<D, kFmt>;
-  constexpr int kKOff = (D / 4) * T::kBits / 8, kVOff = T::kE * T::kBits / 8;
-  load_words<T::kKWords>(buf + r * L::kStride + kKOff * c, br.k);
+  constexpr int kKOff = (D / 4) * T::kBits / 8, kVOffR = T::kE * T::kBits / 8;
+  load_words<T::kKWords>(buf + r * L::kStrideK + kKOff * c, br.k);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) load_words<T::kVWords>(buf + L::kHalf + (4 * c + e) * L::kStride + kVOff * r, br.v[e]);
+  for (int e = 0; e < 4; ++e)
+    load_words<T::kVWords>(buf + L::kVOff + (4 * c + e) * L::kStrideV + kVOffR * r, br.v[e]);
+}
+
+typedef short lds_short4_t __attribute__((ext_vector_type(4)));
+
+// A bf16 block's K registers (load_block_lds) and its P.V operands by
+// transpose reads, in the transposed tile layout; tokens at or past `valid`
+// get V = 0 (their slots may hold NaN).
+template <int D>
+__device__ __forceinline__ void load_block_lds_tr(BlockRegs<D, kFmtBf16>& br, VOperands<D, kFmtBf16>& vo,
+                                                  const uint8_t* buf, int valid, int r, int c) {
+  using T = Tile<D, kFmtBf16>;
+  using L = WideLayout<D, kFmtBf16>;
+  load_words<T::kKWords>(buf + r * L::kStrideK + (D / 4) * 2 * c, br.k);
+  const uint8_t* vrow = buf + L::kVOff + (4 * c + (r >> 2)) * L::kStrideV + 8 * (r & 3);
+#pragma unroll
+  for (int nn = 0; nn < T::kE; ++nn) {
+    typedef __attribute__((address_space(3))) lds_short4_t* lds_ptr;
+    vo.v[nn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(vrow + 32 * nn));
+  }
+  if (valid < kBlockTokens) {
+#pragma unroll
+    for (int nn = 0; nn < T::kE; ++nn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * c + i >= valid) vo.v[nn][i] = 0;
+  }
 }
 
 template <int D, int kFmt>
@@ -388,7 +454,7 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
     const int prow = pidx / L::kPiecesPerRow, pcol = pidx % L::kPiecesPerRow;
     is_v[k] = half != 0;
     src_off[k] = (int64_t)prow * L::kRowBytes + pcol * 16;
-    lds_off[k] = half * L::kHalf + prow * L::kStride + pcol * 16;
+    lds_off[k] = half ? L::kVOff + prow * L::kStrideV + pcol * 16 : prow * L::kStrideK + pcol * 16;
   }
   // A block's pieces, with its scales taken while its id is in the window
   // (the window may move on before the block is folded in).
@@ -456,13 +522,12 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
           if (p < npairs && has_item && i < it_hi) {
             const int t0 = i * kBlockTokens;
             const bool two = i + 1 < it_hi;           // (it_hi <= hi)
-            BlockRegs<D, kFmt> b0, b1;
-            load_block_lds<D, kFmt>(b0, pbuf(p), r, c);
-            load_block_lds<D, kFmt>(b1, pbuf(p) + L::kBuf, r, c);
             const int valid0 = min(kBlockTokens, it.kv_len - t0);
             const int valid1 = two ? min(kBlockTokens, it.kv_len - t0 - kBlockTokens) : 0;
-            const VOperands<D, kFmt> v0 = make_voperands<D, kFmt>(b0, valid0, c);
-            const VOperands<D, kFmt> v1 = make_voperands<D, kFmt>(b1, valid1, c);
+            BlockRegs<D, kFmt> b0, b1;
+            VOperands<D, kFmt> v0, v1;
+            load_block_lds_tr<D>(b0, v0, pbuf(p), valid0, r, c);
+            load_block_lds_tr<D>(b1, v1, pbuf(p) + L::kBuf, valid1, r, c);
             if (second) {
               step_pair_cols2(hs[0], hs[1], b0, b1, v0, v1, valid0, valid1, horizon[0] - t0,
                               horizon[0] - t0 - kBlockTokens, horizon[1] - t0, horizon[1] - t0 - kBlockTokens,
@@ -516,7 +581,7 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
     }
   }
   if (!has_item || ncols <= 0) return;
-  store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, stage);
+  store_item_tiles<D, kFmt, kTiles, wide_transposed<kFmt>()>(a, it, hs, row, ncols, second, g, lane, stage);
 }
 
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k over a merge row's

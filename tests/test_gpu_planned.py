@@ -128,6 +128,29 @@ def test_wide_groups_past_64_blocks(kv):
     assert err <= TOL[kv], err
 
 
+@pytest.mark.parametrize("d,hq,hkv,kv,nseq", [(64, 32, 8, "bf16", 4), (64, 32, 8, "fp8", 4),
+                                               (128, 32, 8, "bf16", 1), (64, 16, 4, "bf16", 1)])
+def test_wide_groups_head_dims_and_cut_runs(d, hq, hkv, kv, nseq):
+    """Wide groups at head_dim 64 and 128; with one sequence the groups alone
+    would not fill the device, so their block runs are cut into pieces whose
+    partial records are merged (the records' path out of a wide group).
+    With four sequences (8 KV heads) every run is whole and each group
+    writes its outputs directly.  Every new token of the first and last
+    sequence checked in full."""
+    wl, dw, want = _multi_query_case(f"wide-d{d}-n{nseq}", 206 + d + nseq, [1500] * nseq, [512] * nseq, hq, hkv,
+                                     d, kv)
+    out, info = _run(dw, wl)
+    assert info.num_wide_groups > 0 and info.num_wgs == 0
+    assert (info.num_merge_rows > 0) == (nseq == 1)
+    got = out_to_f64(out)
+    rows = np.concatenate([np.arange(wl.q_start[b], wl.q_start[b + 1]) for b in sorted({0, nseq - 1})])
+    err = float(np.abs(got[rows] - want[rows]).max())
+    log(f"wide d={d} kv={kv} seqs={nseq}: groups={info.num_wide_groups} merge rows={info.num_merge_rows} "
+        f"max abs error {err:.3e}")
+    assert np.isfinite(got[rows]).all()
+    assert err <= TOL[kv], err
+
+
 def test_decode_through_a_plan_matches_oracle():
     wl = W.make_workload(name="plan-decode", seed=204, context_lens=[1, 17, 600, 1500, 33], num_q_heads=32,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
