@@ -243,7 +243,8 @@ int pa_decode_append(void* out, const void* q, pa_dtype q_dtype,
  * every device it runs on until the process ends.  Calls whose scratch
  * (pa_decode_workspace_size) exceeds it return PA_ERR_WORKSPACE before any
  * launch: every automatic (balanced) split fits; a partition grid fits when
- * num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes does.
+ * num_seqs * num_q_heads * records * (head_dim + 2) * 4 bytes does, a record
+ * covering 4 partitions for a BF16 query and 1 for F32.
  * The call allocates nothing and records no timing events.  All calls on
  * one device share that device's array: calls that may overlap on one
  * device (other streams, other threads) race and must be serialised by the

@@ -32,8 +32,11 @@ __device__ __forceinline__ int clamp_context(const DecodeArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Partition grid: one workgroup of 4 waves per (partition, KV head, sequence);
-// wave w takes the partition's blocks w, w+4, ... and the waves merge in LDS.
+// Partition grid: one workgroup of 4 waves per (group of 4 consecutive
+// partitions, KV head, sequence); wave w folds in partition 4 * group + w
+// (up to 32 blocks of 16 tokens) and the waves merge their partitions by
+// log-sum-exp in LDS, so one partial record (or the output, when the group
+// covers the whole sequence) leaves per group of 4 partitions.
 
 template <int D, int kFmt>
 __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a) {
@@ -43,36 +46,33 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
   __shared__ float lds_l[kPartWaves][16];
   __shared__ f32x4_t lds_acc[kPartWaves][kE][64];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int grp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, c = lane >> 4;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int P = a.partition_tokens;
 
   const int ctx = clamp_context(a, b);
-  const int nparts = (ctx + P - 1) / P;
+  const int ngroups = (ctx + kPartWaves * P - 1) / (kPartWaves * P);
   const int64_t head0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   if (ctx == 0) {
-    if (part == 0)
+    if (grp == 0)
       for (int i = threadIdx.x; i < G * D; i += kPartThreads) out[head0 * D + i] = 0;
     return;
   }
-  const int t0 = part * P;
-  if (t0 >= ctx) return;
-  const int n = min(P, ctx - t0);
-  const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
-  const int nw = wave < nblk ? (nblk - wave + kPartWaves - 1) / kPartWaves : 0;   // blocks of this wave
+  if (grp >= ngroups) return;                           // (every wave of the workgroup)
+  const int t0 = (grp * kPartWaves + wave) * P;         // this wave's partition
+  const int n = max(0, min(P, ctx - t0));
+  const int nw = (n + kBlockTokens - 1) / kBlockTokens; // its blocks (<= 32)
 
   HeadState<D, kFmt> hs;
   hs.begin(reinterpret_cast<const uint16_t*>(a.q), head0, G, r, c);
-  // physical ids (and fp8 scales) of this wave's blocks: lane j holds block j
+  // physical ids (and fp8/int4 scales) of this wave's blocks: lane j holds block j
   int my_blk = 0;
   float my_ks = 1.0f, my_vs = 1.0f;
   if (lane < nw) {
-    my_blk = clamp_block(
-        a.block_tables[(int64_t)b * a.max_blocks_per_seq + t0 / kBlockTokens + wave + kPartWaves * lane],
-        a.num_blocks);
+    my_blk = clamp_block(a.block_tables[(int64_t)b * a.max_blocks_per_seq + t0 / kBlockTokens + lane], a.num_blocks);
     if constexpr (kFmt != kFmtBf16) {
       my_ks = a.k_scale[(int64_t)my_blk * a.num_kv_heads + g];
       my_vs = a.v_scale[(int64_t)my_blk * a.num_kv_heads + g];
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
       sc *= __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_ks), i));
       vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_vs), i));
     }
-    const int valid = min(kBlockTokens, n - (wave + kPartWaves * i) * kBlockTokens);
+    const int valid = min(kBlockTokens, n - i * kBlockTokens);
     hs.step(br, valid, sc, vs, c);
   };
 
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
     }
   }
 
-  // ---- wave totals, then the 4-wave merge through LDS
+  // ---- wave totals, then the 4 partitions' log-sum-exp merge through LDS
   const float lw = hs.total_l();
   if (c == 0) {
     lds_m[wave][r] = hs.m;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
   float L = 0.0f, wt[kPartWaves];
 #pragma unroll
   for (int w = 0; w < kPartWaves; ++w) {
-    wt[w] = __builtin_amdgcn_exp2f(mw[w] - M);   // waves without blocks have m = -inf -> 0
+    wt[w] = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - M);   // partitions past the context weigh nothing
     L += wt[w] * lds_l[w][r];
   }
   float o[4 * kE];
@@ -140,10 +140,10 @@ __global__ __launch_bounds__(kPartThreads) void decode_mfma_kernel(DecodeArgs a)
   if (r >= G) return;
   const int64_t row = head0 + r;
   const int d0 = (D / 4) * c;
-  if (nparts == 1) {
+  if (ngroups == 1) {
     store_bf16_run<D>(out + row * D, d0, o, 1.0f / L);
   } else {
-    const int64_t wr = row * a.num_parts + part;
+    const int64_t wr = row * a.num_recs + grp;
     store_f32_run<D>(a.ws_acc + wr * D, d0, o);
     if (c == 0) {
       a.ws_m[wr] = M;
@@ -598,7 +598,7 @@ int kv_format(pa_dtype cache_dtype) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_recs, a.num_kv_heads, a.num_seqs);   // a record per group of kPartWaves partitions
   const int f = kv_format(a.cache_dtype);
 #define PA_LAUNCH(D_, F_) hipLaunchKernelGGL((decode_mfma_kernel<D_, F_>), grid, dim3(kPartThreads), 0, stream, a)
   if (a.head_dim == 128) {

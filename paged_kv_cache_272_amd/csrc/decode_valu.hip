@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     for (int j = 0; j < kMaxPer; ++j) {
       const int h = hs + j * kHS;
       if (h < G) {
-        const int64_t r = (head0 + h) * a.num_parts + part;
+        const int64_t r = (head0 + h) * a.num_recs + part;     // (a record per partition here)
         a.ws_acc[r * D + d] = acc[j];
         if (d == 0) { a.ws_m[r] = m_s[h]; a.ws_l[r] = l_s[h]; }
       }
@@ -166,10 +166,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-// Merge: one workgroup per (query head, sequence).  Thread (lp, ch) owns the
-// 4-wide output chunk ch and the partitions lp, lp + P', ... (P' = 256 / (D/4)
-// partition lanes), folded with a running maximum four at a time so their
-// loads are in flight together; the partition lanes are combined in LDS.
+// Merge: one workgroup per (query head, sequence) over its partial records
+// (one per partition from the kernel above; one per group of parts_per_rec
+// partitions from the matrix-core grid).  Thread (lp, ch) owns the 4-wide
+// output chunk ch and the records lp, lp + P', ... (P' = 256 / (D/4) lanes),
+// folded with a running maximum four at a time so their loads are in flight
+// together; the lanes are combined in LDS.
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 constexpr int kMergeThreads = 256;
 
@@ -182,14 +184,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float4 s_acc[kLanesP][kChunks];
   const int h = blockIdx.x, b = blockIdx.y;
   const int ch = threadIdx.x % kChunks, lp = threadIdx.x / kChunks;
-  const int P = a.partition_tokens;
+  const int P = a.partition_tokens * a.parts_per_rec;    // tokens per record
   const int ctx = seq_context(a, b);
-  const int nparts = (ctx + P - 1) / P;
+  const int nparts = (ctx + P - 1) / P;                  // records of this sequence
   if (nparts <= 1) return;            // written by the partition kernel
   const int64_t row = (int64_t)b * a.num_q_heads + h;
-  const float* m = a.ws_m + row * a.num_parts;
-  const float* l = a.ws_l + row * a.num_parts;
-  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + row * a.num_parts * D);
+  const float* m = a.ws_m + row * a.num_recs;
+  const float* l = a.ws_l + row * a.num_recs;
+  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + row * a.num_recs * D);
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int p0 = lp; p0 < nparts; p0 += 4 * kLanesP) {

@@ -57,26 +57,35 @@ struct WorkspaceLayout {
   bool balanced = false;
   int32_t partition_tokens = 0;
   int32_t num_parts = 1;
+  int32_t parts_per_rec = 1, num_recs = 1;   // partition grid: records of parts_per_rec partitions
   int32_t num_wgs = 0, waves_per_wg = 0, head_groups = 0;
   size_t bytes = 0;
   size_t m_off = 0, l_off = 0, acc_off = 0, start_off = 0;  // in 4-byte words
 };
 
-// Partition grid: partial rows (sequence, query head, partition).
+// Partition grid: partial rows (sequence, query head, record), a record per
+// parts_per_rec consecutive partitions (4 for the matrix-core kernel, whose
+// waves each take one partition; 1 for the fp32 kernel).
 WorkspaceLayout partition_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                                 int32_t partition_tokens) {
+                                 int32_t partition_tokens, int32_t parts_per_rec) {
   WorkspaceLayout w;
   w.partition_tokens = partition_tokens > 0 ? partition_tokens : auto_partition(max_context_len);
   const int32_t parts = (max_context_len + w.partition_tokens - 1) / w.partition_tokens;
   w.num_parts = parts < 1 ? 1 : parts;
-  if (w.num_parts <= 1) return w;
-  const size_t sec = workspace_section_floats(num_seqs, num_q_heads, w.num_parts);
+  w.parts_per_rec = parts_per_rec;
+  w.num_recs = (w.num_parts + parts_per_rec - 1) / parts_per_rec;
+  if (w.num_recs <= 1) return w;
+  const size_t sec = workspace_section_floats(num_seqs, num_q_heads, w.num_recs);
   w.m_off = 0;
   w.l_off = sec;
   w.acc_off = 2 * sec;
-  w.bytes = (2 * sec + align_floats((size_t)num_seqs * num_q_heads * w.num_parts * head_dim)) * sizeof(float);
+  w.bytes = (2 * sec + align_floats((size_t)num_seqs * num_q_heads * w.num_recs * head_dim)) * sizeof(float);
   return w;
 }
+
+// Partitions per partial record in the partition grid: the matrix-core
+// kernel (bf16 query) merges the 4 partitions of a workgroup itself.
+int32_t parts_per_record(pa_dtype q_dtype) { return q_dtype == PA_DTYPE_F32 ? 1 : 4; }
 
 // Balanced split: partial rows (workgroup, slot 0/1, query head), plus the
 // per-sequence unit starts.  One wave per KV head, at most 8 waves per
@@ -206,7 +215,7 @@ PA_EXPORT int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_hea
   const int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                     partition_tokens);
   if (st != PA_OK) return st;
-  return partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).partition_tokens;
+  return partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens, 1).partition_tokens;
 }
 
 PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -215,8 +224,8 @@ PA_EXPORT size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
       PA_OK)
     return 0;
   // the automatic choice depends on the query type, which this query does not
-  // take: report enough for either split
-  size_t bytes = partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens).bytes;
+  // take: report enough for either split (a record per partition is the larger grid)
+  size_t bytes = partition_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens, 1).bytes;
   if (use_balanced(PA_DTYPE_BF16, num_seqs, partition_tokens)) {
     for (pa_dtype cd : {PA_DTYPE_BF16, PA_DTYPE_INT4}) {   // (nor the cache type: the larger of the two shapes)
       const size_t b2 = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, cd).bytes;
@@ -258,7 +267,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   const WorkspaceLayout w = use_balanced(q_dtype, num_seqs, partition_tokens)
                                 ? balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype)
                                 : partition_layout(num_seqs, num_q_heads, head_dim, max_context_len,
-                                                   partition_tokens);
+                                                   partition_tokens, parts_per_record(q_dtype));
   if (need_only) {
     *need_only = w.bytes;
     return PA_OK;
@@ -289,6 +298,8 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   a.num_blocks = num_blocks;
   a.partition_tokens = w.partition_tokens;
   a.num_parts = w.num_parts;
+  a.parts_per_rec = w.parts_per_rec;
+  a.num_recs = w.num_recs;
   a.balanced = w.balanced ? 1 : 0;
   a.num_wgs = w.num_wgs;
   a.waves_per_wg = w.waves_per_wg;
@@ -313,7 +324,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   const hipError_t e1 = w.balanced ? launch_decode_mfma_balanced(a, s) : launch_decode_partitions(a, s);
   if (e1 != hipSuccess) return PA_ERR_LAUNCH;
   if (rec) (void)hipEventRecord(rec->mid, s);
-  const bool merge = w.balanced || w.num_parts > 1;
+  const bool merge = w.balanced || w.num_recs > 1;
   if (merge) {
     const hipError_t e2 = w.balanced ? launch_decode_merge_balanced(a, s) : launch_decode_merge(a, s);
     if (e2 != hipSuccess) return PA_ERR_LAUNCH;

@@ -43,10 +43,12 @@ struct CopyBlocksArgs {
 // Everything the decode kernels read.
 //
 // Two work splits share the same per-block arithmetic:
-//  * partition grid (`balanced == 0`): one workgroup per (partition of
-//    `partition_tokens` tokens, KV head, sequence).  Workspace rows are
-//    indexed (sequence, query head, partition):
-//      ws_m, ws_l [num_seqs * num_q_heads * num_parts], ws_acc [... * D];
+//  * partition grid (`balanced == 0`): partitions of `partition_tokens`
+//    tokens; a workgroup per (record, KV head, sequence), a record covering
+//    `parts_per_rec` consecutive partitions (the matrix-core kernel: 4, one
+//    per wave, merged in LDS; the fp32 kernel: 1).  Workspace rows are
+//    indexed (sequence, query head, record):
+//      ws_m, ws_l [num_seqs * num_q_heads * num_recs], ws_acc [... * D];
 //  * balanced (`balanced == 1`): `num_wgs` workgroups; workgroup x takes an
 //    equal, contiguous slice of the list of (sequence, 16-token block) units
 //    laid end to end, one wave per KV head.  A sequence cut by a slice edge
@@ -75,7 +77,7 @@ struct DecodeArgs {
   const void* v_new;
   int32_t append;
   int32_t max_blocks_per_seq, max_context_len, num_seqs, num_q_heads, num_kv_heads;
-  int32_t head_dim, num_blocks, partition_tokens, num_parts;
+  int32_t head_dim, num_blocks, partition_tokens, num_parts, parts_per_rec, num_recs;
   int32_t balanced, num_wgs, waves_per_wg, head_groups;
   float scale_log2;  // scale * log2(e): logits are kept in the base-2 domain
   pa_dtype q_dtype, cache_dtype;

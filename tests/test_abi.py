@@ -92,7 +92,7 @@ def test_decode_validation(kw, status):
 
 def noalloc_call(**kw):
     args = dict(out=FAKE, q=FAKE, q_dtype=BF16, k=FAKE, v=FAKE, cache_dtype=BF16, ks=None, vs=None,
-                bt=FAKE, mb=8192, cl=FAKE, max_ctx=131072, b=8, hq=64, hkv=8, d=128, nb=100000, scale=0.088,
+                bt=FAKE, mb=8192, cl=FAKE, max_ctx=131072, b=32, hq=64, hkv=8, d=128, nb=100000, scale=0.088,
                 part=512)
     args.update(kw)
     return lib_mod.raw_call("pa_decode_noalloc", args["out"], args["q"], args["q_dtype"], args["k"], args["v"],
@@ -102,7 +102,7 @@ def noalloc_call(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(), WS),                           # 8 x 64 heads x 256 partitions x 130 floats: 68 MB > 64 MiB
+    (dict(), WS),                           # 32 x 64 heads x 64 records of 4 partitions x 130 floats: 68 MB
     (dict(d=96), UNSUP),
     (dict(hq=30), SHAPE),
     (dict(out=None), NULL),

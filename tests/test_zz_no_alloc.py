@@ -56,13 +56,13 @@ def test_noalloc_equals_pa_decode_two_calls_second_smaller(kv, part):
 
 
 def test_noalloc_rejects_scratch_beyond_its_array():
-    """The long-context batch through 512-token partitions needs 68 MB of
-    scratch: rejected before any launch (the balanced split fits)."""
-    q = torch.zeros(8, 64, 128, dtype=torch.bfloat16, device="cuda")
+    """32 sequences of 131072 tokens through 512-token partitions need 68 MB
+    of scratch: rejected before any launch (the balanced split fits)."""
+    q = torch.zeros(32, 64, 128, dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros(4, 8, 16, 128, dtype=torch.uint8, device="cuda")
     sc = torch.ones(4, 8, dtype=torch.float32, device="cuda")
-    bt = torch.zeros(8, 8192, dtype=torch.int32, device="cuda")
-    cl = torch.full((8,), 131072, dtype=torch.int32, device="cuda")
+    bt = torch.zeros(32, 8192, dtype=torch.int32, device="cuda")
+    cl = torch.full((32,), 131072, dtype=torch.int32, device="cuda")
     with pytest.raises(pa.PaError) as e:
         pa.pa_decode_noalloc(q, q, kc, kc, bt, cl, 131072, 0.088, sc, sc, 512)
     assert e.value.status == -5
