@@ -244,7 +244,8 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
 // Workgroup x runs the items of slice x in order, one wave per KV head.
 template <int D, int kFmt, int kTiles>
 __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(PlannedArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // (the wave index in a scalar register, so addresses built from it are wave-uniform to the compiler)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = blockIdx.y * a.waves_per_wg + wave;
   if (g >= a.num_kv_heads) return;
   extern __shared__ float s_stage[];           // per wave kStageRows x D floats

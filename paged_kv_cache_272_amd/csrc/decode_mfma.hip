@@ -207,7 +207,6 @@ __device__ __forceinline__ UnitIds unit_ids(const DecodeArgs& a, const int* star
     }
   }
   asm volatile("" : "+v"(id.blk));
-  if constexpr (kScaled) asm volatile("" : "+v"(id.ks), "+v"(id.vs));
   return id;
 }
 
@@ -272,7 +271,9 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
   int* s_ctx = s_dyn + a.num_seqs + 1;
 
   const int x = blockIdx.x, y = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // (the wave index in a scalar register: the KV head and every address
+  // derived from it are then wave-uniform to the compiler too)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, c = lane >> 4;
   const int W = a.waves_per_wg;
   const int B = a.num_seqs;
@@ -349,12 +350,18 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
     float o[4 * kE];
     hs.unpack(o);
     const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;   // rows row0 .. row0+G-1
-    const bool whole = s_start[b] >= u0 && s_start[b + 1] <= u1;
-    const int slot = s_start[b] < u0 ? 0 : 1;
+    // (read into scalar registers: the row addresses below are then a scalar
+    // base plus a lane offset, with nothing per lane to keep across the loop)
+    const int sb = __builtin_amdgcn_readfirstlane(s_start[b]), se = __builtin_amdgcn_readfirstlane(s_start[b + 1]);
+    const bool whole = sb >= u0 && se <= u1;
+    const int slot = sb < u0 ? 0 : 1;
     const int64_t wr0 = ((int64_t)x * 2 + slot) * a.num_q_heads + (int64_t)g * G;
+    // (lane offsets taken fresh here, so the compiler keeps no per-lane
+    // address pairs alive across the loop for these rare stores)
+    const int lr = fresh(r), ll = fresh(lane);
     if (!whole && c == 0 && r < G) {
-      a.ws_m[wr0 + r] = hs.m;
-      a.ws_l[wr0 + r] = L;
+      (a.ws_m + wr0)[lr] = hs.m;
+      (a.ws_l + wr0)[lr] = L;
     }
     for (int rr = 0; rr < G; rr += kStageRows) {
       const int nr = min(kStageRows, G - rr);
@@ -365,13 +372,13 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
         wave_lds_sync();
         const uint4* src = reinterpret_cast<const uint4*>(stage);
         uint4* dst = reinterpret_cast<uint4*>(out + (row0 + rr) * D);
-        for (int pc = lane; pc < nr * D / 8; pc += 64) dst[pc] = src[pc];
+        for (int pc = ll; pc < nr * D / 8; pc += 64) dst[pc] = src[pc];
       } else {
         if (mine) store_f32_run<D>(stage + (r - rr) * D, d0, o);
         wave_lds_sync();
         const float4* src = reinterpret_cast<const float4*>(stage);
         float4* dst = reinterpret_cast<float4*>(a.ws_acc + (wr0 + rr) * D);
-        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = src[pc];
+        for (int pc = ll; pc < nr * D / 4; pc += 64) dst[pc] = src[pc];
       }
     }
   };
@@ -424,9 +431,11 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
         st.row_busy = p.row_staged = true;
         load_new_runs(p.b, st.nk, st.nv);
       }
+      // the block's loads go out before the wait for its scales (which
+      // were loaded after the table entries, one round trip later)
+      load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
       p.ks = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.ks), j));
       p.vs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cur.vs), j));
-      load_block<D, kFmt>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c);
     } else {
       p.ks = p.vs = 1.0f;
       load_block_with_row<D>(p.regs, kbase, vbase, p.blk, a.num_kv_heads, g, r, c, p.off, new_k(p.b), new_v(p.b));

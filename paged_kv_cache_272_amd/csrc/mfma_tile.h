@@ -100,24 +100,31 @@ __device__ __forceinline__ constexpr uint32_t perm_sel(uint32_t b0, uint32_t b1,
   return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
-// Two int4 codes in bytes k0, k1 of x (values 0..15) -> one word of bf16
-// bits 0x43cc (128 + code) for each: the high bytes come from a register
-// holding 0x43 in every byte.
-__device__ __forceinline__ uint32_t int4_pair_to_bf16x2(uint32_t x, uint32_t k0, uint32_t k1) {
-  return __builtin_amdgcn_perm(0x43434343u, x, perm_sel(k0, 4, k1, 4));
+// 0x43004300 | (two codes at bits 0-3 and 16-19 of x): a word of bf16 pairs
+// 128 + code, exactly (bf16 holds every integer up to 256).
+// (One v_and_or_b32: the compiler would split it in two, since gfx950's
+// three-operand encodings take no literal and at most one scalar operand.)
+__device__ __forceinline__ uint32_t int4_halves_to_bf16x2(uint32_t x) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(0x000f000fu), "v"(0x43004300u));
+  return r;
 }
 
-// 8 int4 codes (one word, element 2i in the low nibble of byte i) -> 4 words
-// of bf16 pairs (elements 2i, 2i+1 in word i).
+// 8 int4 codes of one K row (one word, element 2i in the low nibble of byte
+// i) -> 4 words of bf16 pairs holding elements (0,4), (1,5), (2,6), (3,7):
+// one shift and one and-or per word.  The query operand is put in the same
+// order (int4_query_order), so the dot product is unchanged.
 __device__ __forceinline__ void int4x8_to_bf16x8(uint32_t w, uint32_t* out) {
-  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-  // elements 0-3 and 4-7 in order, one code per byte
-  const uint32_t x01 = __builtin_amdgcn_perm(hi, lo, perm_sel(0, 4, 1, 5));
-  const uint32_t x23 = __builtin_amdgcn_perm(hi, lo, perm_sel(2, 6, 3, 7));
-  out[0] = int4_pair_to_bf16x2(x01, 0, 1);
-  out[1] = int4_pair_to_bf16x2(x01, 2, 3);
-  out[2] = int4_pair_to_bf16x2(x23, 0, 1);
-  out[3] = int4_pair_to_bf16x2(x23, 2, 3);
+  out[0] = int4_halves_to_bf16x2(w);
+  out[1] = int4_halves_to_bf16x2(w >> 4);
+  out[2] = int4_halves_to_bf16x2(w >> 8);
+  out[3] = int4_halves_to_bf16x2(w >> 12);
+}
+
+// 8 bf16 query elements in order -> the order int4x8_to_bf16x8 gives a K row.
+__device__ __forceinline__ uint4 int4_query_order(uint4 q) {
+  return make_uint4(__builtin_amdgcn_perm(q.z, q.x, perm_sel(0, 1, 4, 5)), __builtin_amdgcn_perm(q.z, q.x, perm_sel(2, 3, 6, 7)),
+                    __builtin_amdgcn_perm(q.w, q.y, perm_sel(0, 1, 4, 5)), __builtin_amdgcn_perm(q.w, q.y, perm_sel(2, 3, 6, 7)));
 }
 
 // Load `W` 32-bit words from a 4*W-byte aligned address.
@@ -198,11 +205,14 @@ template <int D, int kFmt>
 __device__ __forceinline__ void load_block(BlockRegs<D, kFmt>& br, const uint8_t* kbase, const uint8_t* vbase,
                                            int64_t blk, int num_kv_heads, int g, int r, int c) {
   using T = Tile<D, kFmt>;
-  const int64_t head_base = (blk * num_kv_heads + g) * kBlockTokens;            // token row index
-  load_words<T::kKWords>(kbase + T::bytes((head_base + r) * D + (D / 4) * c), br.k);
+  // (a block base common to the wave plus a 32-bit lane offset: no 64-bit
+  // address per lane to compute or keep)
+  const int64_t head_bytes = T::bytes((blk * num_kv_heads + g) * kBlockTokens * D);
+  const uint8_t* kb = kbase + head_bytes;
+  const uint8_t* vb = vbase + head_bytes;
+  load_words<T::kKWords>(kb + (uint32_t)T::bytes(r * D + (D / 4) * c), br.k);
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    load_words<T::kVWords>(vbase + T::bytes((head_base + 4 * c + e) * D + T::kE * r), br.v[e]);
+  for (int e = 0; e < 4; ++e) load_words<T::kVWords>(vb + (uint32_t)T::bytes((4 * c + e) * D + T::kE * r), br.v[e]);
 }
 
 // The Q^T operand of HeadState::begin as raw registers: query rows
@@ -212,7 +222,7 @@ __device__ __forceinline__ void load_block(BlockRegs<D, kFmt>& br, const uint8_t
 // only waited for where begin_loaded() takes them and zeroes lanes r >= G.
 template <int D>
 __device__ __forceinline__ void load_query(const uint16_t* q, int64_t q_row0, int G, int r, int c, uint4* qw) {
-  const uint16_t* qp = q + (q_row0 + min(r, G - 1)) * D + (D / 4) * c;
+  const uint16_t* qp = q + q_row0 * D + (uint32_t)(min(r, G - 1) * D + (D / 4) * c);
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) qw[i] = reinterpret_cast<const uint4*>(qp)[i];
 }
@@ -229,6 +239,26 @@ struct VOperands {
 template <int D, int kFmt>
 __device__ __forceinline__ VOperands<D, kFmt> make_voperands(const BlockRegs<D, kFmt>& br, int valid, int c) {
   using T = Tile<D, kFmt>;
+  if constexpr (kFmt == kFmtInt4) {
+    VOperands<D, kFmt> vo;
+    // nibble nn of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code.
+    // y01a: bytes 0-1 (codes 0-3) of tokens 0 and 1, one token per 16-bit
+    // half; y01b: bytes 2-3 (codes 4-7); y23a, y23b the same for tokens 2, 3.
+    // Code nn then sits at bits 4*(nn%4) of each half.  (Tokens past `valid`
+    // need no masking here: every code gives a finite value, and their P is 0.)
+    const uint32_t y01a = __builtin_amdgcn_perm(br.v[1][0], br.v[0][0], perm_sel(0, 1, 4, 5));
+    const uint32_t y01b = __builtin_amdgcn_perm(br.v[1][0], br.v[0][0], perm_sel(2, 3, 6, 7));
+    const uint32_t y23a = __builtin_amdgcn_perm(br.v[3][0], br.v[2][0], perm_sel(0, 1, 4, 5));
+    const uint32_t y23b = __builtin_amdgcn_perm(br.v[3][0], br.v[2][0], perm_sel(2, 3, 6, 7));
+#pragma unroll
+    for (int nn = 0; nn < T::kE; ++nn) {
+      const int sh = 4 * (nn % 4);
+      const uint32_t lo = int4_halves_to_bf16x2((nn < 4 ? y01a : y01b) >> sh);
+      const uint32_t hi = int4_halves_to_bf16x2((nn < 4 ? y23a : y23b) >> sh);
+      vo.v[nn] = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+    }
+    return vo;
+  }
   uint32_t vw[4][T::kVWords];
   if (valid < kBlockTokens) {
 #pragma unroll
@@ -242,31 +272,6 @@ __device__ __forceinline__ VOperands<D, kFmt> make_voperands(const BlockRegs<D, 
       for (int w = 0; w < T::kVWords; ++w) vw[e][w] = br.v[e][w];
   }
   VOperands<D, kFmt> vo;
-  if constexpr (kFmt == kFmtInt4) {
-    // nibble nn of the 4 tokens' words -> [t0 t1 | t2 t3] as bf16 of 128 + code.
-    // Even nn are low nibbles, odd nn high ones.  x[h][k]: codes of bytes
-    // 2k', 2k'+1 (k' = k mod 2) interleaved over tokens 0, 1 (k < 2) or 2, 3.
-    uint32_t x[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t n4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) n4[e] = (h ? vw[e][0] >> 4 : vw[e][0]) & 0x0f0f0f0fu;
-      x[h][0] = __builtin_amdgcn_perm(n4[1], n4[0], perm_sel(0, 4, 1, 5));
-      x[h][1] = __builtin_amdgcn_perm(n4[1], n4[0], perm_sel(2, 6, 3, 7));
-      x[h][2] = __builtin_amdgcn_perm(n4[3], n4[2], perm_sel(0, 4, 1, 5));
-      x[h][3] = __builtin_amdgcn_perm(n4[3], n4[2], perm_sel(2, 6, 3, 7));
-    }
-#pragma unroll
-    for (int nn = 0; nn < T::kE; ++nn) {
-      const int h = nn & 1, byte = nn / 2;          // code byte `byte` of each token's word
-      const int k = byte / 2, b = 2 * (byte % 2);   // its interleaved word and position there
-      const uint32_t lo = int4_pair_to_bf16x2(x[h][k], b, b + 1);
-      const uint32_t hi = int4_pair_to_bf16x2(x[h][k + 2], b, b + 1);
-      vo.v[nn] = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
-    }
-    return vo;
-  }
 #pragma unroll
   for (int nn = 0; nn < T::kE; ++nn) {
     uint32_t lo, hi;
@@ -307,8 +312,9 @@ struct HeadState {
   float nm;      // -m, or 0 while m = -inf: the offset of the FMA that forms relative logits
   float thr;     // a relative logit above this moves the reference: kLazyMax, or -inf while m = -inf
   float qbias;   // int4: 136 * (sum of this lane's query column): removed from every logit
-  bool qbias_pending = false;   // int4: qbias still to be taken (begin_row)
-  float vbias;   // int4: sum over blocks of V scale * (sum of the block's bf16 P), rescaled like acc
+  bool query_pending = false;   // int4: query still to be reordered and summed (begin_row)
+  float vbias;   // int4: sum over blocks of V scale * (sum of the bf16 P of this lane's tokens),
+                 // rescaled like acc; the column's total is the sum over its 4 lanes
 
   // Q^T operand for query rows q_row0 .. q_row0+G-1 (lane r < G), d chunk (D/32)*c + i.
   __device__ __forceinline__ void begin(const uint16_t* q, int64_t q_row0, int G, int r, int c) {
@@ -320,7 +326,7 @@ struct HeadState {
       qop[i] = __builtin_bit_cast(bf16x8_t, w);
     }
     reset();
-    set_qbias();
+    take_query();
   }
 
   // Start a run from the words load_query() fetched (lanes r >= G get zeros).
@@ -328,26 +334,31 @@ struct HeadState {
 #pragma unroll
     for (int i = 0; i < T::kKSteps; ++i) qop[i] = __builtin_bit_cast(bf16x8_t, r < G ? qw[i] : make_uint4(0, 0, 0, 0));
     reset();
-    set_qbias();
+    take_query();
   }
 
   // Q^T operand with an arbitrary query row per column: lane r takes row
   // `row`; a column that will see no token (every step masks it whole) may
   // pass -1 and gets row 0.  Every lane issues the same loads and nothing
   // here uses their values, so they are waited for at the first step (the
-  // int4 query sum is taken there too).
+  // int4 reordering and query sum are done there too).
   __device__ __forceinline__ void begin_row(const uint16_t* q, int64_t row, int c) {
     const uint16_t* qp = q + (row < 0 ? 0 : row) * D + (D / 4) * c;
 #pragma unroll
     for (int i = 0; i < T::kKSteps; ++i) qop[i] = __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4*>(qp)[i]);
     reset();
-    qbias_pending = true;
+    query_pending = kInt4;
   }
 
-  // int4: 136 times the column's query sum (the 4 lane groups hold D/4 each)
-  __device__ __forceinline__ void set_qbias() {
+  // int4: put the query operand in the element order of the K operand
+  // (int4x8_to_bf16x8) and take 136 times the column's query sum (the 4 lane
+  // groups hold D/4 each).
+  __device__ __forceinline__ void take_query() {
     qbias = 0.0f;
     if constexpr (kInt4) {
+#pragma unroll
+      for (int i = 0; i < T::kKSteps; ++i)
+        qop[i] = __builtin_bit_cast(bf16x8_t, int4_query_order(__builtin_bit_cast(uint4, qop[i])));
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < T::kKSteps; ++i)
@@ -389,6 +400,7 @@ struct HeadState {
   template <bool kCols>
   __device__ __forceinline__ void step_impl(const BlockRegs<D, kFmt>& br, const VOperands<D, kFmt>& vo, int valid,
                                             int col_valid, float sc, float vs, int c) {
+    ready();
     // ---- S^T = K . Q^T
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -405,6 +417,16 @@ struct HeadState {
     fold<4>(x);
     const short4_t pop = probs(x, vs);
     pv(vo, pop, vs);
+  }
+
+  // Before a QK product: the query work begin_row deferred (int4).
+  __device__ __forceinline__ void ready() {
+    if constexpr (kInt4) {
+      if (query_pending) {
+        take_query();
+        query_pending = false;
+      }
+    }
   }
 
   // The K operand of QK MFMA step st (K rows as bf16 pairs), the same for
@@ -428,12 +450,6 @@ struct HeadState {
   // s * sc - m in one FMA (int4: also less 136 times the query sum, the
   // bias the MFMA saw).
   __device__ __forceinline__ void rel_logits(const f32x4_t& s, float sc, float* x) {
-    if constexpr (kInt4) {
-      if (qbias_pending) {
-        set_qbias();
-        qbias_pending = false;
-      }
-    }
     const float off = kInt4 ? __builtin_fmaf(-qbias, sc, nm) : nm;
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(s[j], sc, off);
@@ -488,9 +504,12 @@ struct HeadState {
     const uint2 pbits = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
     if constexpr (kInt4) {
       // the P.V MFMA sees V + 136: keep V scale * (sum of the bf16 P it used) to take off at the end
-      const float ps = (bf16_bits_to_f32(pbits.x & 0xffffu) + bf16_bits_to_f32(pbits.x >> 16)) +
-                       (bf16_bits_to_f32(pbits.y & 0xffffu) + bf16_bits_to_f32(pbits.y >> 16));
-      vbias = __builtin_fmaf(sum_xor16(sum_xor32(ps)), vs, vbias);
+      // (this lane's 4 tokens, two dot products with (1, 1); the lanes are summed at the end)
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+      const float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pbits.y), ones,
+                                                       __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pbits.x), ones, 0.0f, false),
+                                                       false);
+      vbias = __builtin_fmaf(ps, vs, vbias);
     }
     return __builtin_bit_cast(short4_t, pbits);
   }
@@ -513,7 +532,7 @@ struct HeadState {
   // int4: take the V bias out of acc itself (for callers that read acc directly)
   __device__ __forceinline__ void settle() {
     if constexpr (kInt4) {
-      const float vb = kInt4Bias * vbias;
+      const float vb = kInt4Bias * sum_xor16(sum_xor32(vbias));
 #pragma unroll
       for (int t = 0; t < kE; ++t) acc[t] -= vb;
       vbias = 0.0f;
@@ -522,7 +541,7 @@ struct HeadState {
 
   // Output run of this lane: d = (D/4)*c + kE*j + n  ->  o[kE*j + n].
   __device__ __forceinline__ void unpack(float* o) const {
-    const float vb = kInt4 ? kInt4Bias * vbias : 0.0f;
+    const float vb = kInt4 ? kInt4Bias * sum_xor16(sum_xor32(vbias)) : 0.0f;
 #pragma unroll
     for (int nn = 0; nn < kE; ++nn)
 #pragma unroll
@@ -539,6 +558,8 @@ __device__ __forceinline__ void step_cols2(HeadState<D, kFmt>& ha, HeadState<D, 
                                            const VOperands<D, kFmt>& vo, int valid, int col_valid_a, int col_valid_b,
                                            float sc, float vs, int c) {
   using H = HeadState<D, kFmt>;
+  ha.ready();
+  hb.ready();
   f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int st = 0; st < Tile<D, kFmt>::kKSteps; ++st) {
@@ -609,6 +630,14 @@ __device__ __forceinline__ void step_pair_cols2(HeadState<D, kFmtBf16>& ha, Head
     ha.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pa, ha.acc[nn], 0, 0, 0);
     hb.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb, hb.acc[nn], 0, 0, 0);
   }
+}
+
+// The same value, which the compiler must take as computed at this point
+// (an empty asm statement): an address built from it cannot be hoisted and
+// kept in registers across a loop.
+__device__ __forceinline__ int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Finished rows leave a wave through LDS, this many rows per pass.
