@@ -22,10 +22,9 @@ PagedAttention", section 四, the ``kv_cache_dtype`` knob, which is said to
 roughly double the batch) and compare FP16 / FP8 / INT4 KV in an exercise
 ("推理优化", section 五, exercise 1: INT4 about 4x the concurrency); the
 e4m3 variant, round-to-nearest-even, saturation at +-448, and the int4
-layout above are the readings of them taken here.  Parity unpinned by the
-pages on which variant and layout: the pins check these functions against
-the format definitions (and torch's float8_e4m3fn cast), not against
-anything the pages fix.
+layout above are the readings of them taken here.  The pages fix neither
+the variant nor the layout; the pins check these functions against the
+format definitions (exhaustively) and torch's float8_e4m3fn cast.
 """
 from __future__ import annotations
 

@@ -23,10 +23,9 @@ What it computes, and where that is stated:
 * GQA: several query heads share one KV head ("推理优化" section 五,
   exercise 3: 64 query heads, 8 KV heads).  The pages do not fix which query
   heads share which KV head; this reference takes consecutive groups:
-  query head h reads KV head ``h // (Hq / Hkv)``.  Parity unpinned by the
-  pages on this point: the mapping is a convention, shared with the kernels
-  by specification only (the pins check the attention itself, for this
-  mapping).
+  query head h reads KV head ``h // (Hq / Hkv)``.  The pages do not fix
+  the mapping; it is a convention shared with the kernels by specification,
+  and the pins check the attention itself for this mapping.
 * fp8 KV: codes times one float scale per (block, KV head); the scale is
   applied to the decoded code values before attention.
 
