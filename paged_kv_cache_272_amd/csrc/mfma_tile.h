@@ -582,56 +582,6 @@ __device__ __forceinline__ void step_cols2(HeadState<D, kFmt>& ha, HeadState<D, 
   hb.pv(vo, pb, vs);
 }
 
-// Fold two consecutive blocks (32 tokens) of a bf16 cache into two tiles
-// of columns at once: one running-max update per 32 tokens instead of two,
-// and the P.V products as 16x16x32 MFMAs whose K index k = 8c + j runs
-// over tokens 4c + j of the first block (j < 4) and 4c + j - 4 of the
-// second, which is how the lane's P values and both blocks' V operands
-// already lie.  valid1 = 0 when the second block is past the run (its
-// operands must still be in range; they are masked whole).
-template <int D>
-__device__ __forceinline__ void step_pair_cols2(HeadState<D, kFmtBf16>& ha, HeadState<D, kFmtBf16>& hb,
-                                                const BlockRegs<D, kFmtBf16>& b0, const BlockRegs<D, kFmtBf16>& b1,
-                                                const VOperands<D, kFmtBf16>& v0, const VOperands<D, kFmtBf16>& v1,
-                                                int valid0, int valid1, int cva0, int cva1, int cvb0, int cvb1,
-                                                float sc, int c) {
-  using H = HeadState<D, kFmtBf16>;
-  f32x4_t sa0 = {0.0f, 0.0f, 0.0f, 0.0f}, sb0 = sa0, sa1 = sa0, sb1 = sa0;
-#pragma unroll
-  for (int st = 0; st < Tile<D, kFmtBf16>::kKSteps; ++st) {
-    const bf16x8_t k0 = H::k_operand(b0, st), k1 = H::k_operand(b1, st);
-    sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, ha.qop[st], sa0, 0, 0, 0);
-    sb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, hb.qop[st], sb0, 0, 0, 0);
-    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, ha.qop[st], sa1, 0, 0, 0);
-    sb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, hb.qop[st], sb1, 0, 0, 0);
-  }
-  float xa[8], xb[8];
-  ha.rel_logits(sa0, sc, xa);
-  ha.rel_logits(sa1, sc, xa + 4);
-  hb.rel_logits(sb0, sc, xb);
-  hb.rel_logits(sb1, sc, xb + 4);
-  // one wave-uniform test for the context end and both tiles' horizons in both blocks
-  if (valid0 < kBlockTokens || valid1 < kBlockTokens ||
-      __ballot(cva0 < kBlockTokens || cva1 < kBlockTokens || cvb0 < kBlockTokens || cvb1 < kBlockTokens) != 0) {
-    H::hide_tokens(xa, min(valid0, cva0), c);
-    H::hide_tokens(xa + 4, min(valid1, cva1), c);
-    H::hide_tokens(xb, min(valid0, cvb0), c);
-    H::hide_tokens(xb + 4, min(valid1, cvb1), c);
-  }
-  ha.template fold<8>(xa);
-  hb.template fold<8>(xb);
-  const short4_t pa0 = ha.probs(xa, 1.0f), pa1 = ha.probs(xa + 4, 1.0f);
-  const short4_t pb0 = hb.probs(xb, 1.0f), pb1 = hb.probs(xb + 4, 1.0f);
-  const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pa0, pa1, 0, 1, 2, 3, 4, 5, 6, 7));
-  const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pb0, pb1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-  for (int nn = 0; nn < Tile<D, kFmtBf16>::kE; ++nn) {
-    const bf16x8_t v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0.v[nn], v1.v[nn], 0, 1, 2, 3, 4, 5, 6, 7));
-    ha.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pa, ha.acc[nn], 0, 0, 0);
-    hb.acc[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb, hb.acc[nn], 0, 0, 0);
-  }
-}
-
 // The same value, which the compiler must take as computed at this point
 // (an empty asm statement): an address built from it cannot be hoisted and
 // kept in registers across a loop.
