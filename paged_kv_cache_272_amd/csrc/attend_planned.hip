@@ -550,11 +550,11 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
 
   if constexpr (kFmt == kFmtBf16) {
     // bf16: blocks go in pairs (step_pair_cols2), kAheadPairs pairs in
-    // flight per thread, two LDS buffers of a pair each.  Step p folds pair p
-    // in from LDS, having issued the loads of pair p + kAheadPairs, and
-    // writes pair p + 1 (loaded kAheadPairs - 1 steps ago) to the other
-    // buffer.  Past the run's end the loads fetch copies of its last block,
-    // so every step issues the same loads.
+    // flight per thread, two LDS buffers of a pair each.  Step p issues the
+    // loads of pair p + kAheadPairs, writes pair p + 1 (loaded kAheadPairs - 1
+    // steps ago) to the other buffer, and folds pair p in from LDS (the
+    // writes drain while it computes).  Past the run's end the loads fetch
+    // copies of its last block, so every step issues the same loads.
     constexpr int kAheadPairs = 2;
     auto pbuf = [&](int p) { return s_wide + (p & 1) * 2 * L::kBuf; };
     const int npairs = (hi - lo + 1) / 2;
@@ -577,6 +577,7 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
         for (int k = 0; k < kAheadPairs; ++k) {
           const int p = p0 + k, i = lo + 2 * p;
           load_pair(ring[k], p + kAheadPairs);
+          if (p + 1 < npairs) store_pair(p + 1, ring[(k + 1) % kAheadPairs]);
           if (p < npairs && has_item && i < it_hi) {
             const int t0 = i * kBlockTokens;
             const bool two = i + 1 < it_hi;           // (it_hi <= hi)
@@ -595,7 +596,6 @@ __global__ __launch_bounds__(64 * kWideTiles, 2) void attend_wide_kernel(Planned
               if (two) hs[0].step_cols(b1, v1, valid1, horizon[0] - t0 - kBlockTokens, a.scale_log2, 1.0f, c);
             }
           }
-          if (p + 1 < npairs) store_pair(p + 1, ring[(k + 1) % kAheadPairs]);
           lds_barrier();
         }
       }
