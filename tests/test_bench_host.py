@@ -76,3 +76,31 @@ def test_source_hash_follows_the_kernel_sources(tmp_path, monkeypatch):
     # every workload's dominant kernel has a stored source list
     assert set(bench.KERNELS) >= {"decode_8b", "decode_70b", "long_ctx_fp8", "shared_prefix_32x8", "verify4_8b",
                                   "chunked_prefill", "decode_8b_int4"}
+
+
+def test_cpu_baseline_counts_every_sequence_once_per_call_and_reports_its_threads():
+    """The CPU baseline's threads take sequences in turn: every call's bytes
+    are counted once, the sequence index cycles over the batch, and `cores`
+    is the thread count it ran with."""
+    import threading
+    import types
+    bench = _bench()
+    seen, lock = [], threading.Lock()
+
+    def one(b):
+        with lock:
+            seen.append(b)
+        return 1000 + b
+
+    fake = types.SimpleNamespace(cpu_prepare=lambda: None, cpu_one=one, num_seqs=5, cpu_kind="fake")
+    rec = bench.cpu_baseline(fake, 0.3, threads=3)
+    assert rec["cores"] == 3 and rec["kind"] == "oracle" and rec["value"] > 0
+    assert all(0 <= b < 5 for b in seen) and len(seen) >= 5
+    # the reported rate is the summed bytes of exactly the calls made (both
+    # figures are rounded in the record: 1% covers that)
+    elapsed = len(seen) / rec["seqs_per_s"]
+    total = sum(1000 + b for b in seen)
+    assert abs(rec["value"] * 1e9 * elapsed - total) <= 1e-2 * total
+    # sequences are handed out in order, so over any 5 consecutive calls each index appears once
+    counts = [seen.count(b) for b in range(5)]
+    assert max(counts) - min(counts) <= 1 + 3    # (threads may finish their last call out of order)
