@@ -45,7 +45,7 @@ def _check(wl, partition_tokens):
     assert err <= TOL[wl.kv_dtype]
 
 
-@pytest.mark.parametrize("kv,part", [("bf16", 0), ("fp8", 0), ("bf16", 256)])
+@pytest.mark.parametrize("kv,part", [("bf16", 0), ("fp8", 0), ("int4", 0), ("bf16", 256)])
 def test_noalloc_equals_pa_decode_two_calls_second_smaller(kv, part):
     big = W.make_workload(name="noalloc-big", seed=501, context_lens=config2_lengths(np.random.default_rng(5), 64),
                           num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv)
