@@ -1,5 +1,5 @@
-// Paged decode on the matrix cores (gfx950 MFMA), bf16 query with a bf16 or
-// e4m3 KV cache.
+// Paged decode on the matrix cores (gfx950 MFMA), bf16 query with a bf16,
+// e4m3 or int4 KV cache.
 //
 // What is computed is the attention of "系统级优化…" section 3.1 for one
 // query token per sequence, over K/V gathered page by page through the block

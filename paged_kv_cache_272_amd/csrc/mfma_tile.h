@@ -22,8 +22,10 @@
 //        Tile n covers d = (D/16)*r + n, so lane (r, c) ends up holding the
 //        contiguous output run d in [(D/4)c, (D/4)(c+1)) of column r.
 // e4m3 codes are widened to bf16 exactly (every e4m3 value is a bf16
-// value); the per-(block, head) scales multiply the logits (K) and the
-// probabilities fed to P.V (V).
+// value); int4 codes become the bf16 value 128 + code (one and-or per pair
+// of codes), and the 136-times bias terms this adds are taken off per
+// column.  The per-(block, head) scales multiply the logits (K) and the
+// block's fp32 P.V product (V).
 #pragma once
 
 #include "pa_device.h"
