@@ -3,6 +3,7 @@ coverage of every query column's causal run, record routing, XCD-aware item
 order, and the plan executed on the CPU with the oracle's float64 primitives
 against the oracle's direct result."""
 import ctypes
+import math
 
 import numpy as np
 import pytest
@@ -93,7 +94,7 @@ def check_slices(plan, info):
         assert max(loads) - min(loads) <= 1
         reads += sum(loads)
     nxt = n_sliced
-    for item0, n, lo, hi in wide:
+    for item0, n, lo, hi in sorted(wide.tolist()):
         assert item0 == nxt and 1 <= n <= 8 and lo < hi
         sl = slice(item0, item0 + n)
         assert np.all(it["seq"][sl] == it["seq"][item0]) and np.all(it["blk_lo"][sl] == lo)
@@ -101,6 +102,25 @@ def check_slices(plan, info):
         reads += int(hi - lo)
         nxt += n
     assert nxt == info.num_items and reads == info.block_reads
+    check_wide_order(wide, info)
+
+
+def check_wide_order(wide, info):
+    """The wide groups run longest first within each chunk of gcd(groups,
+    per_xcd) groups, where per_xcd = ceil(groups * KV heads / 8) workgroups go
+    to one XCD, and the chunks hold the groups they held in item order: every
+    group keeps the XCD it would have had unsorted."""
+    ng = len(wide)
+    if ng < 2:
+        return
+    per_xcd = -(-ng * info.num_kv_heads // 8)
+    chunk = math.gcd(ng, per_xcd)
+    length = wide[:, 3] - wide[:, 2]
+    for c0 in range(0, ng, chunk):
+        part = wide[c0:c0 + chunk]
+        assert np.all(np.diff(length[c0:c0 + chunk]) <= 0), "not longest first within a chunk"
+        in_order = np.sort(wide[:, 0])[c0:c0 + chunk]
+        assert np.array_equal(np.sort(part[:, 0]), in_order), "a group left its chunk"
 
 
 def test_default_slices_fill_the_device():
@@ -187,8 +207,30 @@ def test_prefill_chunk_goes_to_wide_groups():
     check_coverage(plan, info, _q_start(q_lens), ctxs, bt, 4)
     # a group's run ends at its last item's horizon: chunk tokens 32g .. 32g+31 see up to 3584 + 32(g+1)
     wide = unpack_plan(plan, info)["wide"]
-    assert sorted(int(h) for h in wide[:16, 3]) == [(3584 + 32 * (k + 1)) // 16 for k in range(16)]
-    assert info.block_reads == 4 * sum(int(h) for h in wide[:16, 3])
+    assert sorted(int(h) for h in wide[:, 3]) == sorted(4 * [(3584 + 32 * (k + 1)) // 16 for k in range(16)])
+    assert np.all(wide[:, 2] == 0) and info.block_reads == sum(int(h) for h in wide[:, 3])
+    # 64 groups x 8 heads: one head's 64 groups per XCD, so all 64 run longest first
+    assert np.all(np.diff(wide[:, 3]) <= 0) and wide[0, 3] == 256 and wide[-1, 3] == 226
+
+
+@pytest.mark.parametrize("hkv,nseq", [(8, 4), (2, 4), (1, 2), (1, 3), (16, 2), (8, 3)])
+def test_wide_groups_run_longest_first_within_their_xcd(hkv, nseq):
+    """Causal chunks give groups of different lengths (cut into pieces when
+    the groups alone would not fill the device); they are ordered longest
+    first within chunks of gcd(groups, ceil(groups * KV heads / 8)), so each
+    XCD starts its longest runs first and keeps the groups it had."""
+    ctxs, q_lens = [4096] * nseq, [512] * nseq
+    plan, info = pa.pa_plan_attention(np.array(ctxs), 4 * hkv, hkv, 128, q_start=_q_start(q_lens))
+    check_slices(plan, info)                       # includes the order within chunks
+    wide = unpack_plan(plan, info)["wide"]
+    ng = len(wide)
+    chunk = math.gcd(ng, -(-ng * hkv // 8))
+    length = wide[:, 3] - wide[:, 2]
+    if chunk > 1:
+        unsorted_len = length[np.argsort(wide[:, 0], kind="stable")]
+        moved = any(not np.array_equal(length[c:c + chunk], unsorted_len[c:c + chunk]) for c in range(0, ng, chunk))
+        assert moved or np.all(length == length[0]) or all(
+            np.all(np.diff(unsorted_len[c:c + chunk]) <= 0) for c in range(0, ng, chunk))
 
 
 def test_short_prefill_wide_groups_are_cut_into_pieces():
