@@ -341,7 +341,9 @@ typedef struct pa_plan_info {
  * columns, at least 4 tiles of 32) goes to wide groups instead: up to 4 of
  * its 32-column items, one workgroup per KV head, every block read once
  * into LDS for all of them; their block runs are split into pieces only
- * when the groups alone would not fill the device.  `plan` receives
+ * when the groups alone would not fill the device, and the groups are
+ * ordered longest run first within the groups that share an XCD (the
+ * earlier-started of two workgroups on a CU runs faster).  `plan` receives
  * info->plan_bytes bytes; pass plan = NULL to learn the sizes only.  Errors: NULL_POINTER, BAD_SHAPE
  * (inconsistent lengths, context past the block table), UNSUPPORTED
  * (group > 16, head_dim not 64/128), WORKSPACE (plan_capacity too small).
