@@ -8,6 +8,7 @@ import torch
 import oracle
 import pa_workloads as W
 from gpu_util import TOL, DeviceWorkload, log, oracle_after_write, out_to_f64, quantize_fp8_values, to_dev
+from plan_util import unpack_plan
 
 pytestmark = pytest.mark.gpu
 pa = pytest.importorskip("paged_kv_cache_272_amd")
@@ -101,6 +102,37 @@ def test_prefill_chunk_bench_shape():
     err = float(np.abs(out_to_f64(out)[rows] - want[rows]).max())
     log(f"prefill chunk (bench shape): wide groups={info.num_wide_groups} max abs error {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("nseq,ctx,q_len", [(4, 4096, 512), (2, 1500, 256)])
+def test_wide_group_order_does_not_change_the_result(nseq, ctx, q_len):
+    """The planner orders wide groups longest first; the kernel must give the
+    same bits for any order of the groups (each group owns its items, records
+    and output rows).  Whole runs (4 chunks of 512 at 4096: the groups fill
+    the device) and runs cut into pieces merged through records (2 chunks of
+    256 at 1500); the plan's group array reversed and rotated on the host."""
+    wl = W.make_multi_query_workload(name=f"order{ctx}", seed=207, context_lens=[ctx] * nseq, q_lens=[q_len] * nseq,
+                                     num_q_heads=32, num_kv_heads=8, head_dim=128)
+    dw = DeviceWorkload(wl)
+    dw.cache_write(pa)
+    plan, info = pa.pa_plan_attention(wl.context_lens, 32, 8, 128, q_start=wl.q_start)
+    assert info.num_wide_groups > 2 and info.num_wgs == 0
+    assert (info.num_records == 0) == (nseq == 4)
+    outs = []
+    for perm in ("as planned", "reversed", "rotated"):
+        p2 = plan.copy()
+        wide = unpack_plan(p2, info)["wide"]
+        if perm == "reversed":
+            wide[:] = wide[::-1].copy()
+        elif perm == "rotated":
+            wide[:] = np.roll(wide, 5, axis=0)
+        out = torch.empty_like(dw.q)
+        log(f"wide group order ctx={ctx}: {perm}, groups={info.num_wide_groups} records={info.num_records}")
+        pa.pa_attend_planned(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, wl.scale, pa.plan_to_device(p2),
+                             info, workspace=None)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
