@@ -167,11 +167,7 @@ __device__ __forceinline__ int slice_of(int u, int U, int n) {
   return (int)(((int64_t)(u + 1) * n + U - 1) / U) - 1;
 }
 
-// Finished rows are staged through LDS kStageRows at a time (a group of up
-// to 16 query heads takes two passes); the stage follows start[] and ctx[]
-// in the dynamic LDS, 16-byte aligned.  LDS per workgroup:
-// 4*(2B+1) + 8 waves * 8 rows * D * 4 bytes <= 32 KB + 32 KB for B <= 4096.
-__host__ __device__ constexpr int balanced_stage_offset_words(int num_seqs) { return (2 * num_seqs + 1 + 3) / 4 * 4; }
+static_assert(kBalancedStageRows == kStageRows, "one staging pass: the same rows on host and device");
 
 struct UnitIds {
   int b, i, blk;       // lane j: the (sequence, logical block, physical block) of unit base + j
@@ -342,10 +338,54 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
   // The G rows a wave finishes are consecutive in `out` and in the
   // workspace, but each lane holds a 16-byte-strided run of one row; stores
   // straight from those registers would split every cache line over many
-  // requests.  The rows go through this wave's LDS stage instead and leave
+  // requests.  The rows go through this wave's LDS outbox instead and leave
   // as whole 16-byte pieces, consecutive lanes writing consecutive pieces.
-  float* stage = reinterpret_cast<float*>(s_dyn + balanced_stage_offset_words(a.num_seqs)) + wave * kStageRows * D;
-  auto finish = [&](int b) {
+  // They leave after the loop (or when the outbox is full), not when the
+  // sequence ends: a store is counted with the loads in vmcnt, so a store
+  // issued inside the loop would make the next unit's wait also wait for
+  // the store to complete.  Entry: 4 header words (row index, low and high
+  // word; 1 = final bf16 rows, 0 = partial rows), then either G rows of D
+  // bf16 (final, normalised) or m[G], l[G] (padded to 4 words) and G rows
+  // of D floats (partial).
+  uint32_t* box = reinterpret_cast<uint32_t*>(s_dyn + balanced_stage_offset_words(a.num_seqs)) + wave * a.out_words;
+  // (int4 stores its rows when each sequence ends: its loop is bound by
+  // vector work, not by the loads a store would delay, and the outbox
+  // writes cost it 1-4%)
+  constexpr bool kDeferRows = kFmt != kFmtInt4;
+  const int ml_words = (2 * G + 3) & ~3;
+  int box_used = 0, box_n = 0;   // words and entries in the outbox (wave-uniform)
+  auto flush = [&]() __attribute__((always_inline)) {
+    if (box_n == 0) return;
+    wave_lds_sync();                         // every lane's entry writes are visible
+    const int ll = fresh(lane);
+    int off = 0;
+    for (int k = 0; k < box_n; ++k) {
+      const uint32_t* e = box + off;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(e[0]), hi = __builtin_amdgcn_readfirstlane(e[1]);
+      const bool whole = __builtin_amdgcn_readfirstlane(e[2]) != 0;
+      const int64_t row0 = (int64_t)(((uint64_t)hi << 32) | lo);
+      if (whole) {
+        const uint4* src = reinterpret_cast<const uint4*>(e + 4);
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row0 * D);
+        for (int pc = ll; pc < G * D / 8; pc += 64) dst[pc] = src[pc];
+        off += 4 + G * D / 2;
+      } else {
+        const float* ml = reinterpret_cast<const float*>(e + 4);
+        if (ll < G) {
+          (a.ws_m + row0)[ll] = ml[ll];
+          (a.ws_l + row0)[ll] = ml[G + ll];
+        }
+        const float4* src = reinterpret_cast<const float4*>(e + 4 + ml_words);
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + row0 * D);
+        for (int pc = ll; pc < G * D / 4; pc += 64) dst[pc] = src[pc];
+        off += 4 + ml_words + G * D;
+      }
+    }
+    box_n = 0;
+    box_used = 0;
+    wave_lds_sync();                         // every read of the entries is done before they are rewritten
+  };
+  auto finish = [&](int b) __attribute__((always_inline)) {
     const float L = hs.total_l();
     float o[4 * kE];
     hs.unpack(o);
@@ -356,6 +396,30 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
     const bool whole = sb >= u0 && se <= u1;
     const int slot = sb < u0 ? 0 : 1;
     const int64_t wr0 = ((int64_t)x * 2 + slot) * a.num_q_heads + (int64_t)g * G;
+    const int words = whole ? 4 + G * D / 2 : 4 + ml_words + G * D;
+    if (kDeferRows && words <= a.out_words) {
+      if (box_used + words > a.out_words) flush();
+      uint32_t* e = box + box_used;
+      const int64_t ri = whole ? row0 : wr0;
+      if (lane == 0) *reinterpret_cast<uint4*>(e) = make_uint4((uint32_t)ri, (uint32_t)((uint64_t)ri >> 32), whole ? 1u : 0u, 0u);
+      if (whole) {
+        if (r < G) store_bf16_run<D>(reinterpret_cast<uint16_t*>(e + 4) + r * D, d0, o, 1.0f / L);
+      } else {
+        float* ml = reinterpret_cast<float*>(e + 4);
+        if (c == 0 && r < G) {
+          ml[r] = hs.m;
+          ml[G + r] = L;
+        }
+        if (r < G) store_f32_run<D>(reinterpret_cast<float*>(e + 4 + ml_words) + r * D, d0, o);
+      }
+      box_used += words;
+      ++box_n;
+      return;
+    }
+    // rows stored now (not deferred, or too large for the outbox: a group
+    // of many query heads), kStageRows rows per pass through the outbox's space
+    if constexpr (kDeferRows) flush();
+    float* stage = reinterpret_cast<float*>(box);
     // (lane offsets taken fresh here, so the compiler keeps no per-lane
     // address pairs alive across the loop for these rare stores)
     const int lr = fresh(r), ll = fresh(lane);
@@ -381,6 +445,7 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
         for (int pc = ll; pc < nr * D / 4; pc += 64) dst[pc] = src[pc];
       }
     }
+    if constexpr (kDeferRows) wave_lds_sync();   // the last pass's reads are done before the outbox is reused
   };
 
   // Table entries of the current 64-unit chunk.
@@ -530,6 +595,7 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
     consume(p1);
   }
   finish(cur_b);
+  if constexpr (kDeferRows) flush();
 }
 
 // Merge for the balanced split.  Sequence b's units are covered by slices
@@ -625,8 +691,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_mfma_balanced(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
-  const size_t lds = ((size_t)balanced_stage_offset_words(a.num_seqs) +
-                      (size_t)a.waves_per_wg * kStageRows * a.head_dim) * sizeof(int);
+  const size_t lds = ((size_t)balanced_stage_offset_words(a.num_seqs) + (size_t)a.waves_per_wg * a.out_words) *
+                    sizeof(int);
   const int f = kv_format(a.cache_dtype);
 #define PA_LAUNCH(D_, F_) hipLaunchKernelGGL((decode_mfma_balanced_kernel<D_, F_>), grid, block, lds, stream, a)
   if (a.head_dim == 128) {

@@ -59,6 +59,7 @@ struct WorkspaceLayout {
   int32_t num_parts = 1;
   int32_t parts_per_rec = 1, num_recs = 1;   // partition grid: records of parts_per_rec partitions
   int32_t num_wgs = 0, waves_per_wg = 0, head_groups = 0;
+  int32_t out_words = 0;                     // balanced: LDS outbox words per wave
   size_t bytes = 0;
   size_t m_off = 0, l_off = 0, acc_off = 0, start_off = 0;  // in 4-byte words
 };
@@ -108,6 +109,30 @@ WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t n
   w.acc_off = 2 * align_floats(rows);
   w.start_off = w.acc_off + align_floats(rows * head_dim);
   w.bytes = (w.start_off + align_floats((size_t)num_seqs + 1)) * sizeof(float);
+  // bf16 and e4m3: each wave keeps the rows it finishes in an LDS outbox and
+  // stores them after its loop.  Its size: room for two partial and two
+  // final entries of this group size, within what one workgroup may take of
+  // the CU's 160 KB at eight waves per CU (less 2 KB for the allocation
+  // granularity and static LDS, at most 64 KB a workgroup) after start[] and
+  // ctx[]; at least one staging pass of kBalancedStageRows rows.  int4: the
+  // deferred stores gained nothing (its loop is bound by vector work, not by
+  // the loads the stores delay) and the outbox writes cost 1-4%, so its rows
+  // are stored when each sequence ends, through one staging pass.
+  const size_t floor_words = (size_t)kBalancedStageRows * head_dim;
+  size_t words = floor_words;
+  if (!int4) {
+    const size_t G = (size_t)(num_q_heads / num_kv_heads);
+    const size_t partial_words = 4 + ((2 * G + 3) & ~(size_t)3) + G * head_dim, final_words = 4 + G * head_dim / 2;
+    const size_t want = (2 * partial_words + 2 * final_words + 3) / 4 * 4;
+    const size_t wgs_per_cu = 8 / (size_t)w.waves_per_wg > 0 ? 8 / (size_t)w.waves_per_wg : 1;
+    size_t budget = ((size_t)160 << 10) / wgs_per_cu - 2048;
+    if (budget > ((size_t)64 << 10)) budget = (size_t)64 << 10;
+    const size_t fixed = (size_t)balanced_lds_fixed_words(num_seqs) * sizeof(int);
+    const size_t room = budget > fixed ? (budget - fixed) / sizeof(int) / (size_t)w.waves_per_wg / 4 * 4 : 0;
+    words = room < want ? room : want;
+    if (words < floor_words) words = floor_words;
+  }
+  w.out_words = (int32_t)words;
   return w;
 }
 
@@ -304,6 +329,7 @@ int decode_impl(void* out, const void* q, pa_dtype q_dtype, const void* k_new, c
   a.num_wgs = w.num_wgs;
   a.waves_per_wg = w.waves_per_wg;
   a.head_groups = w.head_groups;
+  a.out_words = w.out_words;
   a.scale_log2 = scale * kLog2e;
   a.q_dtype = q_dtype;
   a.cache_dtype = cache_dtype;

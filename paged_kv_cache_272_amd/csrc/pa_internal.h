@@ -79,6 +79,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq, max_context_len, num_seqs, num_q_heads, num_kv_heads;
   int32_t head_dim, num_blocks, partition_tokens, num_parts, parts_per_rec, num_recs;
   int32_t balanced, num_wgs, waves_per_wg, head_groups;
+  int32_t out_words;  // balanced: 4-byte LDS words of each wave's outbox of finished rows
   float scale_log2;  // scale * log2(e): logits are kept in the base-2 domain
   pa_dtype q_dtype, cache_dtype;
 };
@@ -107,6 +108,13 @@ hipError_t launch_decode_merge_balanced(const DecodeArgs& a, hipStream_t stream)
 // workgroups, up to 256 VGPRs); an int4 cache, bound by vector work rather
 // than HBM, runs three (4-wave workgroups, three per CU, up to 168 VGPRs).
 constexpr int kBalancedMaxSeqs = 4096;
+// LDS of a balanced-split workgroup: start[B + 1] and ctx[B] (padded to 16
+// bytes, plus 16 words for the kernel's static LDS), then each wave's outbox
+// of finished rows (DecodeArgs::out_words words, at least kBalancedStageRows
+// rows of head_dim floats).
+constexpr int kBalancedStageRows = 8;
+__host__ __device__ constexpr int balanced_stage_offset_words(int num_seqs) { return (2 * num_seqs + 1 + 3) / 4 * 4; }
+__host__ __device__ constexpr int balanced_lds_fixed_words(int num_seqs) { return balanced_stage_offset_words(num_seqs) + 16; }
 constexpr int kBalancedTargetWaves = 2048;
 constexpr int kBalancedMaxWaves = 8;
 constexpr int kBalancedTargetWavesInt4 = 3072;
