@@ -150,6 +150,76 @@ __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const Pla
   }
 }
 
+// The partial records of a wave's items other than its last wait in the
+// wave's LDS outbox and are stored after the last item: a store is counted
+// with the loads in vmcnt, so records stored when an item ends would make
+// the next item's first waits also wait for them.  One entry per item, of
+// fixed size: 8 header words (per tile the first record row, low and high
+// word, then per tile its live columns), then per tile m[16], l[16] and 16
+// rows of D floats.  Rows stored at once (the last item's, a direct item's,
+// or an item that finds the outbox full) are staged through the same LDS
+// after the outbox has been emptied.
+template <int D, int kTiles>
+__host__ __device__ constexpr int box_entry_words() { return 8 + kTiles * (32 + 16 * D); }
+
+template <int D, int kFmt, int kTiles>
+__device__ __forceinline__ void box_item_records(const PlannedArgs& a, const PlanItem& it,
+                                                 const HeadState<D, kFmt> (&hs)[kTiles], int ncols, bool second,
+                                                 int g, int lane, uint32_t* e) {
+  const int r = lane & 15, c = lane >> 4;
+  const int d0 = (D / 4) * c;
+  uint32_t head[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    if (t > 0 && !second) break;
+    const int nt = min(16, ncols - 16 * t);
+    const int64_t rec_row0 = (int64_t)g * a.num_records + clampi(it.rec0 + 16 * t, 0, max(a.num_records - nt, 0));
+    head[2 * t] = (uint32_t)rec_row0;
+    head[2 * t + 1] = (uint32_t)((uint64_t)rec_row0 >> 32);
+    head[4 + t] = (uint32_t)nt;
+    const float L = hs[t].total_l();
+    float o[4 * Tile<D, kFmt>::kE];
+    hs[t].unpack(o);
+    float* ml = reinterpret_cast<float*>(e + 8 + t * (32 + 16 * D));
+    if (c == 0 && r < nt) {
+      ml[r] = hs[t].m;
+      ml[16 + r] = L;
+    }
+    if (r < nt) store_f32_run<D>(ml + 32 + r * D, d0, o);
+  }
+  if (lane == 0) {
+    reinterpret_cast<uint4*>(e)[0] = make_uint4(head[0], head[1], head[2], head[3]);
+    reinterpret_cast<uint4*>(e)[1] = make_uint4(head[4], head[5], head[6], head[7]);
+  }
+}
+
+// Store the outbox's n entries and empty it.
+template <int D, int kTiles>
+__device__ __forceinline__ void box_flush(const PlannedArgs& a, const uint32_t* box, int& n, int lane) {
+  if (n == 0) return;
+  wave_lds_sync();                                    // every lane's entry writes are visible
+  for (int k = 0; k < n; ++k) {
+    const uint32_t* e = box + k * box_entry_words<D, kTiles>();
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int nt = (int)__builtin_amdgcn_readfirstlane(e[4 + t]);
+      if (nt <= 0) continue;
+      const int64_t row0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(e[2 * t + 1]) << 32) |
+                                     __builtin_amdgcn_readfirstlane(e[2 * t]));
+      const float* ml = reinterpret_cast<const float*>(e + 8 + t * (32 + 16 * D));
+      if (lane < nt) {
+        a.ws_m[row0 + lane] = ml[lane];
+        a.ws_l[row0 + lane] = ml[16 + lane];
+      }
+      const float4* src = reinterpret_cast<const float4*>(ml + 32);
+      float4* dst = reinterpret_cast<float4*>(a.ws_acc + row0 * D);
+      for (int pc = lane; pc < nt * D / 4; pc += 64) dst[pc] = src[pc];
+    }
+  }
+  wave_lds_sync();                                    // every read of the entries is done before they are rewritten
+  n = 0;
+}
+
 // One plan item on one wave (KV head g): stream the item's blocks through
 // kTiles MFMA tiles of 16 columns (columns 16t .. 16t+15 in tile t), then
 // write the output or the partial records.  `cur` holds the item's columns
@@ -165,7 +235,7 @@ __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const Pla
 template <int D, int kFmt, int kTiles>
 __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& it, const NextItem<kTiles>& cur,
                                          const PlanItem& next_it, NextItem<kTiles>& nx, int g, int lane,
-                                         float* stage) {
+                                         uint32_t* box, int& box_n, bool last) {
   const int r = lane & 15, c = lane >> 4;
   const int ncols = min(it.ncols, 16 * kTiles);
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -238,7 +308,15 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
   settle_reg(nx.blk);
   if (ncols <= 0) return;
 
-  store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, stage);
+  // records of an item before the wave's last wait in the outbox
+  const bool direct = it.rec0 < 0 || a.num_records <= 0;
+  if (!direct && !last && box_n < a.box_entries) {
+    box_item_records<D, kFmt, kTiles>(a, it, hs, ncols, second, g, lane, box + box_n * box_entry_words<D, kTiles>());
+    ++box_n;
+    return;
+  }
+  box_flush<D, kTiles>(a, box, box_n, lane);
+  store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, reinterpret_cast<float*>(box));
 }
 
 // Workgroup x runs the items of slice x in order, one wave per KV head.
@@ -248,11 +326,13 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = blockIdx.y * a.waves_per_wg + wave;
   if (g >= a.num_kv_heads) return;
-  extern __shared__ float s_stage[];           // per wave kStageRows x D floats
+  // per wave: an outbox of box_entries entries, or kStageRows x D floats if larger
+  extern __shared__ uint32_t s_box[];
   const int k0 = clampi(a.wg_start[blockIdx.x], 0, a.num_items);
   const int k1 = clampi(a.wg_start[blockIdx.x + 1], k0, a.num_items);
   if (k0 >= k1) return;
-  float* stage = s_stage + wave * kStageRows * D;
+  uint32_t* box = s_box + wave * max(a.box_entries * box_entry_words<D, kTiles>(), kStageRows * D);
+  int box_n = 0;
   // item headers, 64 at a time: lane j holds item kb + j
   int kb = k0;
   PlanItem mine{0, 0, 0, 0, 0, 0, -1, 0};
@@ -288,10 +368,11 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
       }
       next_it = header(k + 1);
     }
-    run_item<D, kFmt, kTiles>(a, it, cur, next_it, nx, g, lane, stage);
+    run_item<D, kFmt, kTiles>(a, it, cur, next_it, nx, g, lane, box, box_n, k + 1 == k1);
     it = next_it;
     cur = nx;
   }
+  box_flush<D, kTiles>(a, box, box_n, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -706,12 +787,24 @@ __global__ __launch_bounds__(kMergeThreads) void attend_planned_merge_kernel(Pla
 
 }  // namespace
 
-hipError_t launch_attend_planned(const PlannedArgs& a, hipStream_t stream) {
+hipError_t launch_attend_planned(const PlannedArgs& a_in, hipStream_t stream) {
+  PlannedArgs a = a_in;
   const dim3 grid(a.num_wgs, a.head_groups);
   const dim3 block(64 * a.waves_per_wg);
   const int f = a.cache_dtype == PA_DTYPE_FP8_E4M3 ? kFmtFp8 : (a.cache_dtype == PA_DTYPE_INT4 ? kFmtInt4 : kFmtBf16);
   const int tiles = a.max_item_columns > 16 ? 2 : 1;
-  const size_t lds = (size_t)a.waves_per_wg * kStageRows * a.head_dim * sizeof(float);
+  // the outbox: up to two record entries per wave, the workgroup within
+  // 158 KB of LDS (about 2048 waves over the device: 8 waves per CU)
+  const size_t entry = (size_t)(a.head_dim == 128 ? (tiles == 2 ? box_entry_words<128, 2>() : box_entry_words<128, 1>())
+                                                  : (tiles == 2 ? box_entry_words<64, 2>() : box_entry_words<64, 1>())) *
+                       sizeof(float);
+  const size_t stage_bytes = (size_t)kStageRows * a.head_dim * sizeof(float);
+  const size_t budget = ((size_t)158 << 10) / (size_t)(a.waves_per_wg < 8 ? 8 : a.waves_per_wg);   // per wave
+  size_t entries = budget / entry;
+  if (entries > 2) entries = 2;
+  a.box_entries = (int32_t)entries;
+  const size_t per_wave = entries * entry > stage_bytes ? entries * entry : stage_bytes;
+  const size_t lds = (size_t)a.waves_per_wg * per_wave;
 #define PA_LAUNCH(D_, F_, T_) hipLaunchKernelGGL((attend_planned_kernel<D_, F_, T_>), grid, block, lds, stream, a)
 #define PA_LAUNCH_T(D_, F_) do { if (tiles == 2) PA_LAUNCH(D_, F_, 2); else PA_LAUNCH(D_, F_, 1); } while (0)
   if (a.head_dim == 128) {

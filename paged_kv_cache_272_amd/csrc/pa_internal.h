@@ -207,6 +207,7 @@ struct PlannedArgs {
   int32_t num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, num_blocks;
   int32_t waves_per_wg, head_groups;
+  int32_t box_entries;  // sliced items: record entries each wave's LDS outbox holds (set at launch)
   float scale_log2;
   pa_dtype cache_dtype;
 };
