@@ -343,10 +343,11 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
   // They leave after the loop (or when the outbox is full), not when the
   // sequence ends: a store is counted with the loads in vmcnt, so a store
   // issued inside the loop would make the next unit's wait also wait for
-  // the store to complete.  Entry: 4 header words (row index, low and high
-  // word; 1 = final bf16 rows, 0 = partial rows), then either G rows of D
-  // bf16 (final, normalised) or m[G], l[G] (padded to 4 words) and G rows
-  // of D floats (partial).
+  // the store to complete.  Entry: 4 header words (row index or byte
+  // offset, low and high word; kind 1 = final bf16 rows, 0 = partial rows,
+  // 2 = the newest token's bf16 K and V rows for the cache), then G rows of
+  // D bf16 (final, normalised), or m[G], l[G] (padded to 4 words) and G rows
+  // of D floats (partial), or the K row and the V row (D bf16 each).
   uint32_t* box = reinterpret_cast<uint32_t*>(s_dyn + balanced_stage_offset_words(a.num_seqs)) + wave * a.out_words;
   // (int4 stores its rows when each sequence ends: its loop is bound by
   // vector work, not by the loads a store would delay, and the outbox
@@ -362,9 +363,16 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
     for (int k = 0; k < box_n; ++k) {
       const uint32_t* e = box + off;
       const uint32_t lo = __builtin_amdgcn_readfirstlane(e[0]), hi = __builtin_amdgcn_readfirstlane(e[1]);
-      const bool whole = __builtin_amdgcn_readfirstlane(e[2]) != 0;
+      const uint32_t kind = __builtin_amdgcn_readfirstlane(e[2]);
       const int64_t row0 = (int64_t)(((uint64_t)hi << 32) | lo);
-      if (whole) {
+      if (kind == 2) {
+        // the newest token's K and V rows, D bf16 each, at byte offset row0 of both caches
+        const uint4* src = reinterpret_cast<const uint4*>(e + 4);
+        uint8_t* base = ll < D / 8 ? reinterpret_cast<uint8_t*>(const_cast<void*>(a.k_cache))
+                                   : reinterpret_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+        if (ll < D / 4) reinterpret_cast<uint4*>(base + row0)[ll % (D / 8)] = src[ll];
+        off += 4 + D;
+      } else if (kind == 1) {
         const uint4* src = reinterpret_cast<const uint4*>(e + 4);
         uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row0 * D);
         for (int pc = ll; pc < G * D / 8; pc += 64) dst[pc] = src[pc];
@@ -515,7 +523,30 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves, kFmt == kFmtInt4 ? 3 : 1) v
     uint8_t* kw = const_cast<uint8_t*>(kbase);
     uint8_t* vw = const_cast<uint8_t*>(vbase);
     if constexpr (!kScaled) {
-      // the registers already hold the new row (load_block_with_row)
+      // the registers already hold the new row (load_block_with_row); it
+      // goes to the cache with the finished rows after the loop
+      if constexpr (kDeferRows) {
+        constexpr int words = 4 + D;
+        if (words <= a.out_words) {
+          if (box_used + words > a.out_words) flush();
+          uint32_t* e = box + box_used;
+          const int64_t rb = T::bytes((head_base + p.off) * D);   // the row's byte offset, the same in both caches
+          if (lane == 0) *reinterpret_cast<uint4*>(e) = make_uint4((uint32_t)rb, (uint32_t)((uint64_t)rb >> 32), 2u, 0u);
+          if (r == p.off) {
+#pragma unroll
+            for (int w = 0; w < T::kKWords; ++w) e[4 + c * T::kKWords + w] = p.regs.k[w];
+          }
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee)
+            if (4 * c + ee == p.off) {
+#pragma unroll
+              for (int w = 0; w < T::kVWords; ++w) e[4 + D / 2 + r * T::kVWords + w] = p.regs.v[ee][w];
+            }
+          box_used += words;
+          ++box_n;
+          return;
+        }
+      }
       if (r == p.off) store_words<T::kKWords>(kw + T::bytes((head_base + r) * D + d0), p.regs.k);
 #pragma unroll
       for (int e = 0; e < 4; ++e)

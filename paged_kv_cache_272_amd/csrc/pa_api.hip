@@ -110,8 +110,9 @@ WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t n
   w.start_off = w.acc_off + align_floats(rows * head_dim);
   w.bytes = (w.start_off + align_floats((size_t)num_seqs + 1)) * sizeof(float);
   // bf16 and e4m3: each wave keeps the rows it finishes in an LDS outbox and
-  // stores them after its loop.  Its size: room for two partial and two
-  // final entries of this group size, within what one workgroup may take of
+  // stores them after its loop (with the newest token's K and V rows of a
+  // bf16 append).  Its size: room for two partial, two final and two
+  // new-row entries of this group size, within what one workgroup may take of
   // the CU's 160 KB at eight waves per CU (less 2 KB for the allocation
   // granularity and static LDS, at most 64 KB a workgroup) after start[] and
   // ctx[]; at least one staging pass of kBalancedStageRows rows.  int4: the
@@ -123,7 +124,8 @@ WorkspaceLayout balanced_layout(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (!int4) {
     const size_t G = (size_t)(num_q_heads / num_kv_heads);
     const size_t partial_words = 4 + ((2 * G + 3) & ~(size_t)3) + G * head_dim, final_words = 4 + G * head_dim / 2;
-    const size_t want = (2 * partial_words + 2 * final_words + 3) / 4 * 4;
+    const size_t splice_words = 4 + (size_t)head_dim;          // the newest token's K and V rows (bf16)
+    const size_t want = (2 * partial_words + 2 * final_words + 2 * splice_words + 3) / 4 * 4;
     const size_t wgs_per_cu = 8 / (size_t)w.waves_per_wg > 0 ? 8 / (size_t)w.waves_per_wg : 1;
     size_t budget = ((size_t)160 << 10) / wgs_per_cu - 2048;
     if (budget > ((size_t)64 << 10)) budget = (size_t)64 << 10;
