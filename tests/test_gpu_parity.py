@@ -162,8 +162,12 @@ EDGE_CTX = [1, 15, 16, 17, 512, 513]
 @pytest.mark.parametrize("hq,hkv,d,kv", [(4, 4, 64, "f32"), (8, 2, 128, "f32"), (16, 1, 64, "bf16"),
                                          (32, 8, 128, "bf16"), (64, 8, 128, "bf16"), (16, 16, 128, "bf16"),
                                          (64, 8, 128, "fp8"), (8, 8, 64, "fp8"), (32, 8, 128, "int4"),
-                                         (16, 1, 128, "int4")])
+                                         (16, 1, 128, "int4"), (128, 8, 128, "bf16")])
 def test_boundary_lengths_and_groups(hq, hkv, d, kv):
+    """Context lengths around block and partition edges, for several group
+    sizes.  Group 16 at head_dim 128 over 8 KV heads makes a partial entry
+    (16 fp32 rows) larger than a wave's outbox of finished rows: those rows
+    are stored at once through its space while final rows still wait."""
     qd = "f32" if kv == "f32" else "bf16"
     wl = W.make_workload(name="edge", seed=101, context_lens=EDGE_CTX, num_q_heads=hq, num_kv_heads=hkv,
                          head_dim=d, q_dtype=qd, kv_dtype=kv, fp8_mode="values",
@@ -191,10 +195,12 @@ def test_partition_size_invariance(kv):
 
 
 @pytest.mark.parametrize("hq,hkv,d,kv", [(32, 8, 128, "bf16"), (64, 16, 128, "bf16"), (8, 1, 64, "bf16"),
-                                         (64, 8, 128, "fp8")])
+                                         (64, 8, 128, "fp8"), (128, 8, 128, "bf16")])
 def test_many_short_sequences(hq, hkv, d, kv):
     """Balanced split edges: slices holding many whole sequences, sequences cut by
-    slice edges, and more sequences than one scan pass covers."""
+    slice edges, and more sequences than one scan pass covers.  With many
+    sequences a slice the outbox of finished rows fills and is written out
+    in the loop (group 16: after every final entry)."""
     rng = np.random.default_rng(105)
     lens = rng.integers(1, 60, size=1100)
     lens[::37] = rng.integers(300, 900, size=len(lens[::37]))
