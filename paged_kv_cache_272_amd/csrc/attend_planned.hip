@@ -143,8 +143,10 @@ __device__ __forceinline__ void store_item_tiles(const PlannedArgs& a, const Pla
           else store_f32_run<D>(stage + (r - rr) * D, d0, o);
         }
         wave_lds_sync();
+        // (rows past head g's records, only for a plan with fewer records than a tile has columns, are dropped)
+        const int nw = (int)min<int64_t>(nr, (int64_t)(g + 1) * a.num_records - (rec_row0 + rr));
         float4* dst = reinterpret_cast<float4*>(a.ws_acc + (rec_row0 + rr) * D);
-        for (int pc = lane; pc < nr * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
+        for (int pc = lane; pc < nw * D / 4; pc += 64) dst[pc] = reinterpret_cast<const float4*>(stage)[pc];
       }
     }
   }
@@ -195,7 +197,7 @@ __device__ __forceinline__ void box_item_records(const PlannedArgs& a, const Pla
 
 // Store the outbox's n entries and empty it.
 template <int D, int kTiles>
-__device__ __forceinline__ void box_flush(const PlannedArgs& a, const uint32_t* box, int& n, int lane) {
+__device__ __forceinline__ void box_flush(const PlannedArgs& a, const uint32_t* box, int& n, int g, int lane) {
   if (n == 0) return;
   wave_lds_sync();                                    // every lane's entry writes are visible
   for (int k = 0; k < n; ++k) {
@@ -207,13 +209,15 @@ __device__ __forceinline__ void box_flush(const PlannedArgs& a, const uint32_t* 
       const int64_t row0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane(e[2 * t + 1]) << 32) |
                                      __builtin_amdgcn_readfirstlane(e[2 * t]));
       const float* ml = reinterpret_cast<const float*>(e + 8 + t * (32 + 16 * D));
-      if (lane < nt) {
+      // rows past head g's records (only a plan with fewer records than a tile has columns) are dropped
+      const int nw = (int)min<int64_t>(nt, (int64_t)(g + 1) * a.num_records - row0);
+      if (lane < nw) {
         a.ws_m[row0 + lane] = ml[lane];
         a.ws_l[row0 + lane] = ml[16 + lane];
       }
       const float4* src = reinterpret_cast<const float4*>(ml + 32);
       float4* dst = reinterpret_cast<float4*>(a.ws_acc + row0 * D);
-      for (int pc = lane; pc < nt * D / 4; pc += 64) dst[pc] = src[pc];
+      for (int pc = lane; pc < nw * D / 4; pc += 64) dst[pc] = src[pc];
     }
   }
   wave_lds_sync();                                    // every read of the entries is done before they are rewritten
@@ -315,7 +319,7 @@ __device__ __forceinline__ void run_item(const PlannedArgs& a, const PlanItem& i
     ++box_n;
     return;
   }
-  box_flush<D, kTiles>(a, box, box_n, lane);
+  box_flush<D, kTiles>(a, box, box_n, g, lane);
   store_item_tiles<D, kFmt, kTiles>(a, it, hs, row, ncols, second, g, lane, reinterpret_cast<float*>(box));
 }
 
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(64 * kBalancedMaxWaves) void attend_planned_kernel(
     it = next_it;
     cur = nx;
   }
-  box_flush<D, kTiles>(a, box, box_n, lane);
+  box_flush<D, kTiles>(a, box, box_n, g, lane);
 }
 
 // ---------------------------------------------------------------------------
